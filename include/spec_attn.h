@@ -1,0 +1,209 @@
+/*
+ * spec_attn.h -- C ABI of libspecattn, the attention hot path of long-context
+ * speculative decoding on AMD Instinct MI355X (gfx950).
+ *
+ * Three operations, each a set of HIP kernels launched asynchronously on the
+ * caller's stream:
+ *
+ *   spec_attn_draft_sparse  draft-phase attention over a sparse view of the KV
+ *                           cache: attention sink + sliding window, or an
+ *                           explicit budget list of positions.
+ *   spec_attn_verify_tree   verify-phase attention of N speculated tree nodes
+ *                           over the full cache plus their own tree, with
+ *                           padded ragged batches and remapped positions.
+ *   spec_accept_greedy      greedy tree acceptance: an argmax per node, then
+ *                           the longest accepted root path and the bonus token.
+ *
+ * Conventions for every call
+ *   - Tensor arguments are DEVICE pointers owned by the caller.  The library
+ *     never allocates, frees or keeps caller memory; buffers must stay alive
+ *     until the stream work has completed.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *   - Strides are in elements; the head dimension is always contiguous.
+ *   - Every host-visible argument is checked before anything is launched; on
+ *     an error nothing is launched and the call returns a negative status
+ *     with a message available from spec_last_error() (thread-local).
+ *   - Values that live only on the device (cache_len, budget indices,
+ *     parents) are checked by the kernels.  A bad value sets a bit in the
+ *     device error word kept in the workspace, and the affected outputs are
+ *     written as NaN (attention) or -1 (token outputs).  spec_device_status()
+ *     reports and clears that word.
+ *   - Workspace: a caller-allocated device buffer of at least the size the
+ *     matching spec_*_workspace_bytes() returns, zero-filled once before its
+ *     first use.  It may be reused by any later call issued to the same
+ *     stream; calls that overlap in time (different streams) need separate
+ *     workspaces.  Sizes depend only on the arguments, never on the device.
+ *   - dtype SPEC_BF16 is the tuned path (bf16 inputs, fp32 accumulation, bf16
+ *     outputs rounded to nearest-even); SPEC_F32 is a plain fp32 path.
+ *   - head_dim must be 64 or 128.  Query head h reads KV head h / (Hq / Hkv).
+ *
+ * Sources (page title, then the passage):
+ *   [WM] "Windowed-MTP: Removing the Full-Context Draft-KV Tax at Million-Token
+ *        Context" (Pith review), "What carries the argument" and Eq. 1.
+ *   [BD] "BudgetDraft: Acceptance-Aware Multi-View Training for Sparse-KV
+ *        Speculative Decoding" (Pith review), abstract and Figure 2.
+ *   [SM] "SpecMemo: Speculative Decoding is in Your Pocket" (Pith review),
+ *        "What carries the argument" and Figure 9.
+ *   [PV] "SpecPV: Improving Self-Speculative Decoding for Long-Context
+ *        Generation via Partial Verification", section 4.1 "Metrics".
+ */
+#ifndef SPEC_ATTN_H
+#define SPEC_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPEC_ABI_VERSION 1
+
+typedef int32_t spec_status;
+enum {
+  SPEC_OK = 0,
+  SPEC_E_INVALID = -1,       /* bad argument: null pointer, shape, stride, alignment */
+  SPEC_E_UNSUPPORTED = -2,   /* well-formed but outside what this build supports */
+  SPEC_E_WORKSPACE = -3,     /* workspace missing or smaller than required */
+  SPEC_E_HIP = -4,           /* the HIP runtime reported an error */
+  SPEC_E_DEVICE_RANGE = -5   /* a kernel found an out-of-range device value */
+};
+
+/* Element types of q, K, V and out. */
+enum { SPEC_F32 = 0, SPEC_BF16 = 1 };
+
+/* Bits of the device error word (spec_device_status). */
+enum {
+  SPEC_DEV_CACHE_LEN = 1u,   /* cache_len[b] < 0, > capacity, or < n_q_tokens (draft) */
+  SPEC_DEV_INDEX = 2u,       /* a budget index outside [0, cache_len[b]) */
+  SPEC_DEV_PARENT = 4u,      /* parents[i] not in [-1, i) */
+  SPEC_DEV_DEPTH = 8u        /* accepted path longer than max_depth */
+};
+
+typedef struct {
+  int32_t batch;          /* B >= 0 (0 = nothing to do) */
+  int32_t n_q_heads;      /* Hq >= 1 */
+  int32_t n_kv_heads;     /* Hkv >= 1, Hq % Hkv == 0 */
+  int32_t head_dim;       /* D: 64 or 128 */
+  int32_t dtype;          /* SPEC_F32 or SPEC_BF16 */
+  float softmax_scale;    /* finite, > 0; scores are softmax_scale * <q, k> */
+} spec_dims;
+
+/* A K/V pair laid out as [B][Hkv][capacity][D] with arbitrary strides (in
+ * elements) over the first three dimensions; D is contiguous.  K and V share
+ * the strides.  bf16: pointers 16-byte aligned, strides multiples of 8;
+ * fp32: pointers 16-byte aligned, strides multiples of 4. */
+typedef struct {
+  const void* k;
+  const void* v;
+  int64_t stride_b;
+  int64_t stride_h;
+  int64_t stride_t;       /* >= D */
+  int32_t capacity;       /* allocated slots per (b, h); cache_len[b] <= capacity */
+} spec_kv;
+
+/*
+ * Draft attention over a sparse view of the cache ([WM] "What carries the
+ * argument"; [BD] abstract).
+ *
+ * q [B][Tq][Hq][D] contiguous; the Tq >= 1 queries are the last Tq positions
+ * of each sequence, so query t sits at position e_t - 1 with
+ * e_t = cache_len[b] - Tq + t + 1, and never sees a position >= e_t.
+ *
+ * Window mode (idx == NULL): query t attends to the union of the first
+ * n_sink positions and the last `window` positions ending at itself, each
+ * counted once: {j < min(n_sink, e_t)} U {max(0, e_t - window) <= j < e_t}.
+ * n_sink >= 0, window >= 1.  RoPE is already applied to the cached keys.
+ *
+ * Budget mode (idx != NULL): query t attends to the listed positions
+ * idx[b][h'][0..budget) that are < e_t, with h' = kv head (idx_stride_h > 0)
+ * or 0 for every head (idx_stride_h == 0).  Duplicates count as often as
+ * listed.  A listed value outside [0, cache_len[b]) raises SPEC_DEV_INDEX
+ * and poisons that (b, kv head)'s outputs with NaN.  A row that sees no
+ * position gets out = 0 and lse = -inf.  idx is int32, 4-byte aligned.
+ *
+ * out [B][Tq][Hq][D] (dtype), lse [B][Tq][Hq] fp32 natural-log sum-exp of
+ * the scaled scores (optional).  cache_len[b] < Tq raises SPEC_DEV_CACHE_LEN.
+ */
+spec_status spec_attn_draft_sparse(const spec_dims* dims, const void* q, int32_t n_q_tokens,
+                                   const spec_kv* cache, const int32_t* cache_len,
+                                   int32_t n_sink, int32_t window,
+                                   const int32_t* idx, int32_t budget,
+                                   int64_t idx_stride_b, int64_t idx_stride_h,
+                                   void* out, float* lse_or_null,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Tree-masked verify attention ([SM] "What carries the argument", Figure 9).
+ *
+ * q [B][N][Hq][D] contiguous, 1 <= N <= 64 speculated nodes.  parents int32,
+ * [N] (parents_stride_b == 0, shared) or [B][N]: parents[i] = -1 for a child
+ * of the anchor (the last committed token, already in the cache), otherwise
+ * an earlier node (parents[i] < i); anything else raises SPEC_DEV_PARENT and
+ * poisons that sequence's outputs.
+ *
+ * Node i of sequence b attends to every cache slot j < cache_len[b] whose
+ * pad[b][j] is 0 (padding slots score -inf; pad == NULL means no padding),
+ * then to the tree nodes on its root path, itself included.  Tree keys and
+ * values come from `tree` ([B][Hkv][N][D] through its strides; it may alias
+ * the cache slots just past cache_len).  pad is uint8 [B][pad_stride_b],
+ * 4-byte aligned with pad_stride_b % 4 == 0 and >= capacity.
+ *
+ * Outputs: out [B][N][Hq][D] (dtype); lse [B][N][Hq] fp32 (optional);
+ * pos_ids [B][N] int32 (optional) = number of non-padding slots in
+ * [0, cache_len[b]) + depth(i), depth 0 for children of the anchor.
+ */
+spec_status spec_attn_verify_tree(const spec_dims* dims, const void* q, int32_t n_nodes,
+                                  const spec_kv* cache, const int32_t* cache_len,
+                                  const uint8_t* pad_or_null, int64_t pad_stride_b,
+                                  const spec_kv* tree, const int32_t* parents,
+                                  int64_t parents_stride_b,
+                                  void* out, float* lse_or_null, int32_t* pos_ids_or_null,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Greedy tree acceptance ([BD] Figure 2; [WM] losslessness; [PV] 4.1).
+ *
+ * logits fp32 [B][N+1][V] contiguous, 16-byte aligned: row 0 is the
+ * verifier's output at the anchor, row i+1 its output at node i.  The greedy
+ * target of a row is its argmax (ties: smallest index; NaN counts as the
+ * maximum, first NaN wins).  Node i is accepted iff its parent is accepted
+ * (the anchor always is) and draft_tokens[b][i] equals the parent's target.
+ * The result is the deepest accepted node (ties: smallest index):
+ *   accept_len[b]  = its depth + 1, or 0 when no node is accepted;
+ *   accept_path[b] = node ids root-first, -1 padded to max_depth;
+ *   bonus[b]       = the target of the last accepted row (row 0 if none).
+ * A path longer than max_depth raises SPEC_DEV_DEPTH (the first max_depth
+ * entries are written).  1 <= N <= 64; parents as in spec_attn_verify_tree.
+ */
+spec_status spec_accept_greedy(int32_t batch, int32_t n_nodes, int32_t vocab,
+                               const float* logits, const int32_t* draft_tokens,
+                               const int32_t* parents, int64_t parents_stride_b,
+                               int32_t max_depth,
+                               int32_t* accept_len, int32_t* accept_path, int32_t* bonus,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace sizes in bytes (0 on invalid arguments; see spec_last_error).
+ * max_view_len for the draft: min(capacity, n_sink + window + n_q_tokens - 1)
+ * in window mode, the budget in budget mode (a larger value is always safe).
+ * capacity for verify: the cache capacity passed to the call. */
+size_t spec_draft_workspace_bytes(const spec_dims* dims, int32_t n_q_tokens,
+                                  int32_t max_view_len);
+size_t spec_verify_workspace_bytes(const spec_dims* dims, int32_t n_nodes,
+                                   int32_t capacity);
+size_t spec_accept_workspace_bytes(int32_t batch, int32_t n_nodes, int32_t vocab);
+
+/* Waits for `stream`, reads and clears the device error word of `workspace`.
+ * Returns SPEC_OK, SPEC_E_DEVICE_RANGE (bits in *bits_or_null) or
+ * SPEC_E_HIP. */
+spec_status spec_device_status(void* workspace, void* stream, uint32_t* bits_or_null);
+
+const char* spec_status_string(spec_status s);
+const char* spec_last_error(void);
+int32_t spec_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_ATTN_H */

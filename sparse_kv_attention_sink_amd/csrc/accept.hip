@@ -1,0 +1,159 @@
+// Greedy tree acceptance (gfx950).
+//
+// Method: "BudgetDraft: Acceptance-Aware Multi-View Training for Sparse-KV
+// Speculative Decoding" (Pith review), Figure 2: the full-cache verifier
+// produces greedy targets; "Windowed-MTP: Removing the Full-Context Draft-KV
+// Tax at Million-Token Context" (Pith review), losslessness: the target
+// decides every accepted token; "SpecPV: Improving Self-Speculative Decoding
+// for Long-Context Generation via Partial Verification", section 4.1
+// "Metrics": the accept length may be 0.
+//
+// Two kernels.  (1) Split-vocabulary argmax: each block scans a contiguous
+// slice of one logits row with 16-byte loads and reduces (value, index)
+// pairs by shuffles under the rule "larger value wins, NaN beats every
+// number, ties go to the smaller index"; the per-slice winners land in the
+// workspace.  (2) One wavefront per sequence finishes the argmax of every
+// row, then walks the tree in node order (parents precede children).
+#include "dev_common.h"
+
+namespace spec {
+
+struct ArgBest {
+  float v;
+  int i;
+};
+
+// true iff (v1, i1) should win over (v2, i2)
+__device__ __forceinline__ bool arg_better(float v1, int i1, float v2, int i2) {
+  const bool n1 = isnan(v1), n2 = isnan(v2);
+  if (n1 || n2) return n1 && (!n2 || i1 < i2);
+  return v1 > v2 || (v1 == v2 && i1 < i2);
+}
+
+__device__ __forceinline__ void arg_consider(float& bv, int& bi, float v, int i) {
+  if (arg_better(v, i, bv, bi)) {
+    bv = v;
+    bi = i;
+  }
+}
+
+__global__ __launch_bounds__(256) void argmax_partial_kernel(const float* __restrict__ logits,
+                                                             int64_t V, int vsplits, int64_t vchunk,
+                                                             ArgBest* __restrict__ part) {
+  const int row = blockIdx.x / vsplits, sp = blockIdx.x % vsplits;
+  const int tid = threadIdx.x;
+  const float* x = logits + (int64_t)row * V;
+  const int64_t v0 = (int64_t)sp * vchunk;
+  const int64_t v1 = min(V, v0 + vchunk);
+  float bv = -INFINITY;
+  int bi = INT_MAX;
+  // unaligned head, 16-byte body, tail
+  int64_t a0 = v0;
+  const int64_t mis = (reinterpret_cast<uintptr_t>(x + v0) >> 2) & 3;
+  if (mis) a0 = min(v1, v0 + (4 - mis));
+  for (int64_t v = v0 + tid; v < a0; v += 256) arg_consider(bv, bi, x[v], (int)v);
+  const int64_t nvec = (v1 - a0) / 4;
+  const float4* xv = reinterpret_cast<const float4*>(x + a0);
+  for (int64_t k = tid; k < nvec; k += 256) {
+    const float4 f = xv[k];
+    const int base = (int)(a0 + 4 * k);
+    arg_consider(bv, bi, f.x, base);
+    arg_consider(bv, bi, f.y, base + 1);
+    arg_consider(bv, bi, f.z, base + 2);
+    arg_consider(bv, bi, f.w, base + 3);
+  }
+  for (int64_t v = a0 + 4 * nvec + tid; v < v1; v += 256) arg_consider(bv, bi, x[v], (int)v);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const float ov = __shfl_xor(bv, m, 64);
+    const int oi = __shfl_xor(bi, m, 64);
+    arg_consider(bv, bi, ov, oi);
+  }
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  if ((tid & 63) == 0) {
+    sv[tid >> 6] = bv;
+    si[tid >> 6] = bi;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 1; w < 4; ++w) arg_consider(bv, bi, sv[w], si[w]);
+    part[(int64_t)row * vsplits + sp] = ArgBest{bv, bi};
+  }
+}
+
+__global__ __launch_bounds__(64) void accept_walk_kernel(
+    int N, int vsplits, const ArgBest* __restrict__ part, const int32_t* __restrict__ tokens,
+    const int32_t* __restrict__ parents, int64_t par_sb, int max_depth, int32_t* accept_len,
+    int32_t* accept_path, int32_t* bonus, uint32_t* err) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  __shared__ int am[kMaxNodes + 1];
+  __shared__ int par_s[kMaxNodes];
+  for (int r = lane; r <= N; r += 64) {
+    const ArgBest* p = part + ((int64_t)b * (N + 1) + r) * vsplits;
+    float bv = p[0].v;
+    int bi = p[0].i;
+    for (int s = 1; s < vsplits; ++s) arg_consider(bv, bi, p[s].v, p[s].i);
+    am[r] = bi;
+  }
+  bool bad = false;
+  if (lane < N) {
+    const int pr = parents[b * par_sb + lane];
+    par_s[lane] = pr;
+    bad = !(pr >= -1 && pr < lane);
+  }
+  const bool any_bad = __syncthreads_or(bad);
+  if (lane != 0) return;
+  int32_t* path = accept_path + (int64_t)b * max_depth;
+  if (any_bad) {
+    raise_error(err, SPEC_DEV_PARENT);
+    accept_len[b] = -1;
+    bonus[b] = -1;
+    for (int k = 0; k < max_depth; ++k) path[k] = -1;
+    return;
+  }
+  // accepted flags and depths in node order; keep the deepest accepted node
+  uint64_t acc = 0;
+  int depth[kMaxNodes];
+  int best = -1, best_depth = -1;
+  for (int i = 0; i < N; ++i) {
+    const int pr = par_s[i];
+    depth[i] = pr < 0 ? 0 : depth[pr] + 1;
+    const bool parent_ok = pr < 0 || ((acc >> pr) & 1ull);
+    if (parent_ok && tokens[(int64_t)b * N + i] == am[pr + 1]) {
+      acc |= 1ull << i;
+      if (depth[i] > best_depth) {
+        best = i;
+        best_depth = depth[i];
+      }
+    }
+  }
+  const int len = best < 0 ? 0 : best_depth + 1;
+  for (int k = 0; k < max_depth; ++k) path[k] = -1;
+  int j = best;
+  for (int k = len - 1; k >= 0; --k) {
+    if (k < max_depth) path[k] = j;
+    j = par_s[j];
+  }
+  if (len > max_depth) raise_error(err, SPEC_DEV_DEPTH);
+  accept_len[b] = len;
+  bonus[b] = am[best + 1];
+}
+
+hipError_t launch_accept(int B, int N, int V, const float* logits, const int32_t* tokens,
+                         const int32_t* parents, int64_t parents_sb, int max_depth,
+                         int32_t* accept_len, int32_t* accept_path, int32_t* bonus, void* ws,
+                         int vsplits, hipStream_t st, uint32_t* err) {
+  ArgBest* part = reinterpret_cast<ArgBest*>(reinterpret_cast<uint8_t*>(ws) + kHeaderBytes);
+  const int64_t vchunk = cdiv(V, vsplits);
+  const int64_t rows = (int64_t)B * (N + 1);
+  hipLaunchKernelGGL(argmax_partial_kernel, dim3((unsigned)(rows * vsplits)), dim3(256), 0, st,
+                     logits, (int64_t)V, vsplits, vchunk, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(accept_walk_kernel, dim3(B), dim3(64), 0, st, N, vsplits, part, tokens,
+                     parents, parents_sb, max_depth, accept_len, accept_path, bonus, err);
+  return hipGetLastError();
+}
+
+}  // namespace spec

@@ -1,0 +1,407 @@
+// C ABI of libspecattn: argument validation, split planning and launches.
+// Every host-visible argument is checked before the first launch; the
+// kernels check the values that live only on the device.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "spec_internal.h"
+
+namespace spec {
+hipError_t launch_draft_bf16(const AttnArgs& a, hipStream_t st);
+hipError_t launch_verify_bf16(const AttnArgs& a, hipStream_t st);
+hipError_t launch_verify_prep(const AttnArgs& a, const int32_t* parents, int64_t parents_sb,
+                              int32_t* pos_ids, uint64_t* anc_ws, int32_t* bad_ws,
+                              hipStream_t st);
+hipError_t launch_attn_f32(const AttnArgs& a, int mode, hipStream_t st);
+}  // namespace spec
+
+using namespace spec;
+
+namespace {
+
+thread_local std::string g_err;
+
+spec_status fail(spec_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+spec_status hip_fail(hipError_t e, const char* what) {
+  return fail(SPEC_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr int64_t kTargetWaves = 2048;     // 256 CUs x 8 wavefronts
+constexpr int64_t kMaxGrid = 0x7fffffff;
+
+spec_status check_dims(const spec_dims* d) {
+  if (d == nullptr) return fail(SPEC_E_INVALID, "dims is NULL");
+  if (d->batch < 0) return fail(SPEC_E_INVALID, "batch %d < 0", d->batch);
+  if (d->n_q_heads < 1 || d->n_kv_heads < 1)
+    return fail(SPEC_E_INVALID, "head counts must be >= 1 (Hq=%d, Hkv=%d)", d->n_q_heads, d->n_kv_heads);
+  if (d->n_q_heads % d->n_kv_heads != 0)
+    return fail(SPEC_E_INVALID, "Hq=%d is not a multiple of Hkv=%d", d->n_q_heads, d->n_kv_heads);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(SPEC_E_UNSUPPORTED, "head_dim %d (supported: 64, 128)", d->head_dim);
+  if (d->dtype != SPEC_F32 && d->dtype != SPEC_BF16)
+    return fail(SPEC_E_UNSUPPORTED, "dtype %d (supported: SPEC_F32, SPEC_BF16)", d->dtype);
+  if (!(d->softmax_scale > 0.f) || !isfinite(d->softmax_scale))
+    return fail(SPEC_E_INVALID, "softmax_scale must be finite and > 0");
+  return SPEC_OK;
+}
+
+size_t esize(int dtype) { return dtype == SPEC_BF16 ? 2 : 4; }
+
+spec_status check_kv(const spec_kv* kv, const spec_dims* d, const char* name, bool need_cap) {
+  if (kv == nullptr) return fail(SPEC_E_INVALID, "%s is NULL", name);
+  if (kv->k == nullptr || kv->v == nullptr) return fail(SPEC_E_INVALID, "%s.k / %s.v is NULL", name, name);
+  if (!aligned(kv->k, 16) || !aligned(kv->v, 16))
+    return fail(SPEC_E_INVALID, "%s.k / %s.v must be 16-byte aligned", name, name);
+  const int64_t m = d->dtype == SPEC_BF16 ? 8 : 4;
+  if (kv->stride_b < 0 || kv->stride_h < 0 || kv->stride_t < d->head_dim)
+    return fail(SPEC_E_INVALID, "%s strides (%lld, %lld, %lld) invalid for head_dim %d", name,
+                (long long)kv->stride_b, (long long)kv->stride_h, (long long)kv->stride_t, d->head_dim);
+  if (kv->stride_b % m || kv->stride_h % m || kv->stride_t % m)
+    return fail(SPEC_E_INVALID, "%s strides must be multiples of %lld elements", name, (long long)m);
+  if (need_cap && kv->capacity < 0) return fail(SPEC_E_INVALID, "%s.capacity %d < 0", name, kv->capacity);
+  return SPEC_OK;
+}
+
+// ------------------------------------------------------------ planning
+
+Plan draft_plan(const spec_dims* d, int32_t Tq, int64_t max_view) {
+  Plan p;
+  const int G = d->n_q_heads / d->n_kv_heads;
+  p.rows = Tq * G;
+  const int64_t pairs = (int64_t)d->batch * d->n_kv_heads;
+  if (d->dtype == SPEC_BF16) {
+    p.rb = p.rows <= 4 ? 4 : p.rows <= 8 ? 8 : p.rows <= 12 ? 12 : 16;
+    p.n_rb = (int32_t)cdiv(p.rows, p.rb);
+    plan_splits(p, pairs, max_view, 64, 32, kTargetWaves);
+  } else {
+    p.rb = 1;
+    p.n_rb = p.rows;
+    plan_splits(p, pairs, max_view, 64, 64, kTargetWaves);
+  }
+  plan_partials(p, pairs, d->head_dim);
+  return p;
+}
+
+Plan verify_plan(const spec_dims* d, int32_t N, int32_t capacity) {
+  Plan p;
+  const int G = d->n_q_heads / d->n_kv_heads;
+  p.rows = N * G;
+  const int64_t pairs = (int64_t)d->batch * d->n_kv_heads;
+  const int64_t keys = capacity > 0 ? capacity : 1;
+  if (d->dtype == SPEC_BF16) {
+    p.rb = p.rows <= 16 ? 16 : 32;
+    p.n_rb = (int32_t)cdiv(p.rows, p.rb);
+    plan_splits(p, pairs, keys, 256, 32, kTargetWaves);
+  } else {
+    p.rb = 1;
+    p.n_rb = p.rows;
+    plan_splits(p, pairs, keys, 64, 64, kTargetWaves);
+  }
+  plan_partials(p, pairs, d->head_dim);
+  size_t off = p.total;
+  p.anc_off = off;
+  off = align_up(off + (size_t)d->batch * N * sizeof(uint64_t), 256);
+  p.bad_off = off;
+  off = align_up(off + (size_t)d->batch * sizeof(int32_t), 256);
+  p.total = off;
+  return p;
+}
+
+int accept_vsplits(int64_t rows, int64_t V) {
+  int64_t vs = cdiv(kTargetWaves, rows > 0 ? rows : 1);
+  int64_t vmax = V / 4096;
+  if (vmax < 1) vmax = 1;
+  if (vs > vmax) vs = vmax;
+  if (vs < 1) vs = 1;
+  return (int)vs;
+}
+
+size_t accept_bytes(int64_t rows, int vs) {
+  return align_up(kHeaderBytes + (size_t)rows * vs * 8, 256);
+}
+
+int64_t draft_max_view(const spec_kv* cache, int32_t Tq, int32_t n_sink, int32_t window,
+                       const int32_t* idx, int32_t budget) {
+  if (idx != nullptr) return budget;
+  int64_t v = (int64_t)n_sink + window + Tq - 1;
+  return v < cache->capacity ? v : cache->capacity;
+}
+
+}  // namespace
+
+#pragma GCC visibility push(default)
+extern "C" {
+
+int32_t spec_abi_version(void) { return SPEC_ABI_VERSION; }
+
+const char* spec_last_error(void) { return g_err.c_str(); }
+
+const char* spec_status_string(spec_status s) {
+  switch (s) {
+    case SPEC_OK: return "SPEC_OK";
+    case SPEC_E_INVALID: return "SPEC_E_INVALID";
+    case SPEC_E_UNSUPPORTED: return "SPEC_E_UNSUPPORTED";
+    case SPEC_E_WORKSPACE: return "SPEC_E_WORKSPACE";
+    case SPEC_E_HIP: return "SPEC_E_HIP";
+    case SPEC_E_DEVICE_RANGE: return "SPEC_E_DEVICE_RANGE";
+    default: return "unknown status";
+  }
+}
+
+size_t spec_draft_workspace_bytes(const spec_dims* dims, int32_t n_q_tokens, int32_t max_view_len) {
+  if (check_dims(dims) != SPEC_OK) return 0;
+  if (n_q_tokens < 1 || max_view_len < 0) {
+    fail(SPEC_E_INVALID, "n_q_tokens must be >= 1 and max_view_len >= 0");
+    return 0;
+  }
+  return draft_plan(dims, n_q_tokens, max_view_len).total;
+}
+
+size_t spec_verify_workspace_bytes(const spec_dims* dims, int32_t n_nodes, int32_t capacity) {
+  if (check_dims(dims) != SPEC_OK) return 0;
+  if (n_nodes < 1 || n_nodes > kMaxNodes || capacity < 0) {
+    fail(SPEC_E_INVALID, "n_nodes must be in [1, 64] and capacity >= 0");
+    return 0;
+  }
+  return verify_plan(dims, n_nodes, capacity).total;
+}
+
+size_t spec_accept_workspace_bytes(int32_t batch, int32_t n_nodes, int32_t vocab) {
+  if (batch < 0 || n_nodes < 1 || n_nodes > kMaxNodes || vocab < 1) {
+    fail(SPEC_E_INVALID, "need batch >= 0, 1 <= n_nodes <= 64, vocab >= 1");
+    return 0;
+  }
+  const int64_t rows = (int64_t)batch * (n_nodes + 1);
+  return accept_bytes(rows, accept_vsplits(rows, vocab));
+}
+
+spec_status spec_attn_draft_sparse(const spec_dims* dims, const void* q, int32_t n_q_tokens,
+                                   const spec_kv* cache, const int32_t* cache_len,
+                                   int32_t n_sink, int32_t window, const int32_t* idx,
+                                   int32_t budget, int64_t idx_stride_b, int64_t idx_stride_h,
+                                   void* out, float* lse_or_null, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  spec_status st = check_dims(dims);
+  if (st != SPEC_OK) return st;
+  if (n_q_tokens < 1) return fail(SPEC_E_INVALID, "n_q_tokens %d < 1", n_q_tokens);
+  if ((st = check_kv(cache, dims, "cache", true)) != SPEC_OK) return st;
+  if (q == nullptr || out == nullptr || cache_len == nullptr)
+    return fail(SPEC_E_INVALID, "q, out and cache_len must not be NULL");
+  if (!aligned(q, 16) || !aligned(out, 16)) return fail(SPEC_E_INVALID, "q and out must be 16-byte aligned");
+  if (lse_or_null != nullptr && !aligned(lse_or_null, 4)) return fail(SPEC_E_INVALID, "lse must be 4-byte aligned");
+  if (!aligned(cache_len, 4)) return fail(SPEC_E_INVALID, "cache_len must be 4-byte aligned");
+  int mode;
+  if (idx == nullptr) {
+    if (n_sink < 0 || window < 1) return fail(SPEC_E_INVALID, "window mode needs n_sink >= 0 and window >= 1");
+    mode = kDraftWindow;
+  } else {
+    if (budget < 1) return fail(SPEC_E_INVALID, "budget %d < 1", budget);
+    if (idx_stride_b < 0 || idx_stride_h < 0) return fail(SPEC_E_INVALID, "idx strides must be >= 0");
+    if (!aligned(idx, 4)) return fail(SPEC_E_INVALID, "idx must be 4-byte aligned");
+    mode = kDraftGather;
+  }
+  const int64_t max_view = draft_max_view(cache, n_q_tokens, n_sink, window, idx, budget);
+  const Plan p = draft_plan(dims, n_q_tokens, max_view);
+  if (workspace == nullptr || workspace_bytes < p.total)
+    return fail(SPEC_E_WORKSPACE, "workspace of %zu bytes needed (got %zu)", p.total,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  if (!aligned(workspace, 256)) return fail(SPEC_E_INVALID, "workspace must be 256-byte aligned");
+  const int64_t waves = (int64_t)dims->batch * dims->n_kv_heads * p.n_rb * p.splits;
+  if (waves > kMaxGrid) return fail(SPEC_E_UNSUPPORTED, "problem too large for one launch");
+  if (dims->batch == 0) return SPEC_OK;
+
+  AttnArgs a{};
+  a.q = q;
+  a.k = cache->k;
+  a.v = cache->v;
+  a.kb = cache->stride_b;
+  a.kh = cache->stride_h;
+  a.kt = cache->stride_t;
+  a.capacity = cache->capacity;
+  a.cache_len = cache_len;
+  a.B = dims->batch;
+  a.Hq = dims->n_q_heads;
+  a.Hkv = dims->n_kv_heads;
+  a.G = a.Hq / a.Hkv;
+  a.D = dims->head_dim;
+  a.T = n_q_tokens;
+  a.R = p.rows;
+  a.scale_log2 = dims->softmax_scale * kLog2e;
+  a.n_sink = n_sink;
+  a.window = window;
+  a.idx = idx;
+  a.budget = budget;
+  a.idx_sb = idx_stride_b;
+  a.idx_sh = idx_stride_h;
+  a.rb = p.rb;
+  a.n_rb = p.n_rb;
+  a.splits = p.splits;
+  a.chunk = p.chunk;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  a.o_part = reinterpret_cast<float*>(ws + p.o_off);
+  a.lse_part = reinterpret_cast<float*>(ws + p.lse_off);
+  a.out = out;
+  a.lse = lse_or_null;
+  a.err = reinterpret_cast<uint32_t*>(ws);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = dims->dtype == SPEC_BF16 ? launch_draft_bf16(a, s) : launch_attn_f32(a, mode, s);
+  if (e != hipSuccess) return hip_fail(e, "draft launch");
+  if (p.splits > 1) {
+    e = launch_combine(a, dims->dtype, s);
+    if (e != hipSuccess) return hip_fail(e, "combine launch");
+  }
+  return SPEC_OK;
+}
+
+spec_status spec_attn_verify_tree(const spec_dims* dims, const void* q, int32_t n_nodes,
+                                  const spec_kv* cache, const int32_t* cache_len,
+                                  const uint8_t* pad_or_null, int64_t pad_stride_b,
+                                  const spec_kv* tree, const int32_t* parents,
+                                  int64_t parents_stride_b, void* out, float* lse_or_null,
+                                  int32_t* pos_ids_or_null, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  spec_status st = check_dims(dims);
+  if (st != SPEC_OK) return st;
+  if (n_nodes < 1 || n_nodes > kMaxNodes)
+    return fail(n_nodes > kMaxNodes ? SPEC_E_UNSUPPORTED : SPEC_E_INVALID,
+                "n_nodes %d outside [1, 64]", n_nodes);
+  if ((st = check_kv(cache, dims, "cache", true)) != SPEC_OK) return st;
+  if ((st = check_kv(tree, dims, "tree", false)) != SPEC_OK) return st;
+  if (q == nullptr || out == nullptr || cache_len == nullptr || parents == nullptr)
+    return fail(SPEC_E_INVALID, "q, out, cache_len and parents must not be NULL");
+  if (!aligned(q, 16) || !aligned(out, 16)) return fail(SPEC_E_INVALID, "q and out must be 16-byte aligned");
+  if (!aligned(cache_len, 4) || !aligned(parents, 4)) return fail(SPEC_E_INVALID, "cache_len and parents must be 4-byte aligned");
+  if (lse_or_null != nullptr && !aligned(lse_or_null, 4)) return fail(SPEC_E_INVALID, "lse must be 4-byte aligned");
+  if (pos_ids_or_null != nullptr && !aligned(pos_ids_or_null, 4)) return fail(SPEC_E_INVALID, "pos_ids must be 4-byte aligned");
+  if (parents_stride_b != 0 && parents_stride_b < n_nodes)
+    return fail(SPEC_E_INVALID, "parents_stride_b must be 0 (shared) or >= n_nodes");
+  if (pad_or_null != nullptr) {
+    if (!aligned(pad_or_null, 4) || pad_stride_b % 4 != 0 || pad_stride_b < cache->capacity)
+      return fail(SPEC_E_INVALID, "pad must be 4-byte aligned with pad_stride_b %% 4 == 0 and >= capacity");
+  }
+  const Plan p = verify_plan(dims, n_nodes, cache->capacity);
+  if (workspace == nullptr || workspace_bytes < p.total)
+    return fail(SPEC_E_WORKSPACE, "workspace of %zu bytes needed (got %zu)", p.total,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  if (!aligned(workspace, 256)) return fail(SPEC_E_INVALID, "workspace must be 256-byte aligned");
+  const int64_t waves = (int64_t)dims->batch * dims->n_kv_heads * p.n_rb * p.splits;
+  if (waves > kMaxGrid) return fail(SPEC_E_UNSUPPORTED, "problem too large for one launch");
+  if (dims->batch == 0) return SPEC_OK;
+
+  AttnArgs a{};
+  a.q = q;
+  a.k = cache->k;
+  a.v = cache->v;
+  a.kb = cache->stride_b;
+  a.kh = cache->stride_h;
+  a.kt = cache->stride_t;
+  a.capacity = cache->capacity;
+  a.cache_len = cache_len;
+  a.B = dims->batch;
+  a.Hq = dims->n_q_heads;
+  a.Hkv = dims->n_kv_heads;
+  a.G = a.Hq / a.Hkv;
+  a.D = dims->head_dim;
+  a.T = n_nodes;
+  a.R = p.rows;
+  a.scale_log2 = dims->softmax_scale * kLog2e;
+  a.pad = pad_or_null;
+  a.pad_sb = pad_stride_b;
+  a.tk = tree->k;
+  a.tv = tree->v;
+  a.tkb = tree->stride_b;
+  a.tkh = tree->stride_h;
+  a.tkt = tree->stride_t;
+  a.rb = p.rb;
+  a.n_rb = p.n_rb;
+  a.splits = p.splits;
+  a.chunk = p.chunk;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  a.o_part = reinterpret_cast<float*>(ws + p.o_off);
+  a.lse_part = reinterpret_cast<float*>(ws + p.lse_off);
+  uint64_t* anc_ws = reinterpret_cast<uint64_t*>(ws + p.anc_off);
+  int32_t* bad_ws = reinterpret_cast<int32_t*>(ws + p.bad_off);
+  a.anc = anc_ws;
+  a.bad = bad_ws;
+  a.out = out;
+  a.lse = lse_or_null;
+  a.err = reinterpret_cast<uint32_t*>(ws);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_verify_prep(a, parents, parents_stride_b, pos_ids_or_null, anc_ws, bad_ws, s);
+  if (e != hipSuccess) return hip_fail(e, "verify prep launch");
+  e = dims->dtype == SPEC_BF16 ? launch_verify_bf16(a, s) : launch_attn_f32(a, kVerify, s);
+  if (e != hipSuccess) return hip_fail(e, "verify launch");
+  if (p.splits > 1) {
+    e = launch_combine(a, dims->dtype, s);
+    if (e != hipSuccess) return hip_fail(e, "combine launch");
+  }
+  return SPEC_OK;
+}
+
+spec_status spec_accept_greedy(int32_t batch, int32_t n_nodes, int32_t vocab, const float* logits,
+                               const int32_t* draft_tokens, const int32_t* parents,
+                               int64_t parents_stride_b, int32_t max_depth, int32_t* accept_len,
+                               int32_t* accept_path, int32_t* bonus, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (batch < 0) return fail(SPEC_E_INVALID, "batch %d < 0", batch);
+  if (n_nodes < 1 || n_nodes > kMaxNodes)
+    return fail(n_nodes > kMaxNodes ? SPEC_E_UNSUPPORTED : SPEC_E_INVALID, "n_nodes %d outside [1, 64]", n_nodes);
+  if (vocab < 1) return fail(SPEC_E_INVALID, "vocab %d < 1", vocab);
+  if (max_depth < 1) return fail(SPEC_E_INVALID, "max_depth %d < 1", max_depth);
+  if (logits == nullptr || draft_tokens == nullptr || parents == nullptr || accept_len == nullptr ||
+      accept_path == nullptr || bonus == nullptr)
+    return fail(SPEC_E_INVALID, "a required pointer is NULL");
+  if (!aligned(logits, 16)) return fail(SPEC_E_INVALID, "logits must be 16-byte aligned");
+  if (!aligned(draft_tokens, 4) || !aligned(parents, 4) || !aligned(accept_len, 4) ||
+      !aligned(accept_path, 4) || !aligned(bonus, 4))
+    return fail(SPEC_E_INVALID, "int32 arrays must be 4-byte aligned");
+  if (parents_stride_b != 0 && parents_stride_b < n_nodes)
+    return fail(SPEC_E_INVALID, "parents_stride_b must be 0 (shared) or >= n_nodes");
+  const int64_t rows = (int64_t)batch * (n_nodes + 1);
+  const int vs = accept_vsplits(rows, vocab);
+  const size_t need = accept_bytes(rows, vs);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(SPEC_E_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  if (!aligned(workspace, 256)) return fail(SPEC_E_INVALID, "workspace must be 256-byte aligned");
+  if (rows * vs > kMaxGrid) return fail(SPEC_E_UNSUPPORTED, "problem too large for one launch");
+  if (batch == 0) return SPEC_OK;
+  hipError_t e = launch_accept(batch, n_nodes, vocab, logits, draft_tokens, parents, parents_stride_b,
+                               max_depth, accept_len, accept_path, bonus, workspace, vs,
+                               static_cast<hipStream_t>(stream), static_cast<uint32_t*>(workspace));
+  if (e != hipSuccess) return hip_fail(e, "accept launch");
+  return SPEC_OK;
+}
+
+spec_status spec_device_status(void* workspace, void* stream, uint32_t* bits_or_null) {
+  if (workspace == nullptr) return fail(SPEC_E_INVALID, "workspace is NULL");
+  hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  uint32_t bits = 0;
+  e = hipMemcpy(&bits, workspace, sizeof bits, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpy (read error word)");
+  if (bits_or_null) *bits_or_null = bits;
+  if (bits == 0) return SPEC_OK;
+  const uint32_t zero = 0;
+  e = hipMemcpy(workspace, &zero, sizeof zero, hipMemcpyHostToDevice);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpy (clear error word)");
+  return fail(SPEC_E_DEVICE_RANGE, "device range error bits 0x%x", bits);
+}
+
+}  // extern "C"
+#pragma GCC visibility pop

@@ -1,0 +1,173 @@
+"""The C ABI on the CPU: the library loads, exports every function the header
+declares, sizes workspaces without a device, and rejects bad arguments before
+launching anything (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_kv_attention_sink_amd as skg
+from sparse_kv_attention_sink_amd import SpecDims, SpecKV
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spec_attn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(skg.LIB_PATH):
+        pytest.fail("libspecattn.so is not built (python -m sparse_kv_attention_sink_amd.build)")
+    return skg.load()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:spec_status|size_t|const char\*|int32_t)\s+(spec_\w+)\(",
+                                 text, flags=re.M)))
+
+
+def test_header_declares_the_three_operations():
+    fns = header_functions()
+    for name in ("spec_attn_draft_sparse", "spec_attn_verify_tree", "spec_accept_greedy"):
+        assert name in fns
+
+
+def test_every_declared_function_is_exported(lib):
+    fns = header_functions()
+    assert fns == sorted(skg.EXPORTED)
+    for name in fns:
+        assert hasattr(lib, name), name
+
+
+def test_abi_version(lib):
+    assert lib.spec_abi_version() == 1
+    assert lib.spec_status_string(skg.SPEC_E_WORKSPACE) == b"SPEC_E_WORKSPACE"
+
+
+def dims(B=1, Hq=32, Hkv=8, D=128, dtype=skg.SPEC_BF16, scale=0.088):
+    return SpecDims(B, Hq, Hkv, D, dtype, scale)
+
+
+def test_workspace_sizes_are_device_free_and_monotone(lib):
+    d = dims(B=8)
+    a = skg.draft_workspace_bytes(d, 1, 256)
+    b = skg.draft_workspace_bytes(d, 1, 2048)
+    assert 256 <= a <= b and a % 256 == 0
+    v = skg.verify_workspace_bytes(d, 64, 16384)
+    assert v >= 256 + 8 * 64 * 8
+    assert skg.accept_workspace_bytes(8, 64, 128256) >= 256 + 8 * 65 * 8
+    assert skg.draft_workspace_bytes(d, 1, 256) == a          # deterministic
+    assert skg.verify_workspace_bytes(dims(), 65, 100) == 0     # > 64 nodes
+    assert b"n_nodes" in lib.spec_last_error()
+
+
+FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation first
+
+
+def kv(cap=4096, stride_t=128, ptr=FAKE):
+    return SpecKV(ptr, ptr, 8 * cap * 128, cap * 128, stride_t, cap)
+
+
+def draft(lib, d, *, q=FAKE, tq=1, cache=None, sink=4, win=64, idx=None, budget=0, ws=FAKE,
+          wsb=1 << 30, out=FAKE):
+    cache = cache or kv()
+    return lib.spec_attn_draft_sparse(ctypes.byref(d), q, tq, ctypes.byref(cache), FAKE, sink, win,
+                                      idx, budget, 0, 0, out, None, ws, wsb, None)
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(d=dims(Hq=30, Hkv=8)), skg.SPEC_E_INVALID),
+    (dict(d=dims(D=96)), skg.SPEC_E_UNSUPPORTED),
+    (dict(d=dims(dtype=7)), skg.SPEC_E_UNSUPPORTED),
+    (dict(d=dims(scale=0.0)), skg.SPEC_E_INVALID),
+    (dict(d=dims(scale=float("inf"))), skg.SPEC_E_INVALID),
+    (dict(d=dims(B=-1)), skg.SPEC_E_INVALID),
+    (dict(tq=0), skg.SPEC_E_INVALID),
+    (dict(q=None), skg.SPEC_E_INVALID),
+    (dict(q=FAKE + 2), skg.SPEC_E_INVALID),
+    (dict(out=None), skg.SPEC_E_INVALID),
+    (dict(cache=kv(stride_t=64)), skg.SPEC_E_INVALID),
+    (dict(cache=kv(stride_t=132)), skg.SPEC_E_INVALID),
+    (dict(cache=kv(ptr=FAKE + 8)), skg.SPEC_E_INVALID),
+    (dict(cache=kv(cap=-1)), skg.SPEC_E_INVALID),
+    (dict(win=0), skg.SPEC_E_INVALID),
+    (dict(sink=-1), skg.SPEC_E_INVALID),
+    (dict(idx=FAKE, budget=0), skg.SPEC_E_INVALID),
+    (dict(idx=FAKE + 2, budget=16), skg.SPEC_E_INVALID),
+    (dict(ws=None), skg.SPEC_E_WORKSPACE),
+    (dict(wsb=16), skg.SPEC_E_WORKSPACE),
+    (dict(ws=FAKE + 16), skg.SPEC_E_INVALID),
+])
+def test_draft_rejects_bad_arguments(lib, bad, status):
+    d = bad.pop("d", dims())
+    assert draft(lib, d, **bad) == status
+    assert lib.spec_last_error()
+
+
+def verify(lib, d, *, n=5, cache=None, tree=None, parents=FAKE, psb=0, pad=None, pad_sb=0,
+           ws=FAKE, wsb=1 << 30):
+    cache = cache or kv()
+    tree = tree or kv(cap=n)
+    return lib.spec_attn_verify_tree(ctypes.byref(d), FAKE, n, ctypes.byref(cache), FAKE, pad,
+                                     pad_sb, ctypes.byref(tree), parents, psb, FAKE, None, None,
+                                     ws, wsb, None)
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(n=0), skg.SPEC_E_INVALID),
+    (dict(n=65), skg.SPEC_E_UNSUPPORTED),
+    (dict(parents=None), skg.SPEC_E_INVALID),
+    (dict(psb=3), skg.SPEC_E_INVALID),
+    (dict(pad=FAKE, pad_sb=4095), skg.SPEC_E_INVALID),
+    (dict(pad=FAKE, pad_sb=1024), skg.SPEC_E_INVALID),
+    (dict(pad=FAKE + 1, pad_sb=4096), skg.SPEC_E_INVALID),
+    (dict(tree=kv(cap=5, ptr=FAKE + 4)), skg.SPEC_E_INVALID),
+    (dict(wsb=1024), skg.SPEC_E_WORKSPACE),
+])
+def test_verify_rejects_bad_arguments(lib, bad, status):
+    assert verify(lib, dims(), **bad) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((1, 0, 100), skg.SPEC_E_INVALID),
+    ((1, 65, 100), skg.SPEC_E_UNSUPPORTED),
+    ((1, 4, 0), skg.SPEC_E_INVALID),
+    ((-1, 4, 100), skg.SPEC_E_INVALID),
+])
+def test_accept_rejects_bad_arguments(lib, args, status):
+    B, N, V = args
+    st = lib.spec_accept_greedy(B, N, V, FAKE, FAKE, FAKE, 0, 4, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert st == status
+
+
+def test_accept_rejects_bad_pointers(lib):
+    assert lib.spec_accept_greedy(1, 4, 100, FAKE + 4, FAKE, FAKE, 0, 4, FAKE, FAKE, FAKE, FAKE,
+                                  1 << 30, None) == skg.SPEC_E_INVALID
+    assert lib.spec_accept_greedy(1, 4, 100, FAKE, FAKE, FAKE, 0, 0, FAKE, FAKE, FAKE, FAKE,
+                                  1 << 30, None) == skg.SPEC_E_INVALID
+    assert lib.spec_accept_greedy(1, 4, 100, FAKE, FAKE, FAKE, 0, 4, FAKE, FAKE, FAKE, FAKE,
+                                  8, None) == skg.SPEC_E_WORKSPACE
+
+
+def test_device_status_rejects_null(lib):
+    assert lib.spec_device_status(None, None, None) == skg.SPEC_E_INVALID
+
+
+def test_empty_batch_is_a_no_op(lib):
+    """batch = 0 passes validation and launches nothing."""
+    assert draft(lib, dims(B=0)) == skg.SPEC_OK
+    assert verify(lib, dims(B=0)) == skg.SPEC_OK
+    assert lib.spec_accept_greedy(0, 4, 100, FAKE, FAKE, FAKE, 0, 4, FAKE, FAKE, FAKE, FAKE,
+                                  1 << 30, None) == skg.SPEC_OK
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    """No silent fallback: a missing library is an error."""
+    saved = skg._lib._lib
+    skg._lib._lib = None
+    try:
+        with pytest.raises(RuntimeError):
+            skg._lib.load(str(tmp_path / "missing.so"))
+    finally:
+        skg._lib._lib = saved

@@ -1,0 +1,224 @@
+"""GPU parity: the HIP library against the fp64 oracle on the workloads and
+on small ragged shapes that span several tiles.
+
+Bars: attention max-abs error <= 1e-2 for bf16 inputs and <= 2e-5 for fp32
+(plus a relative L2 guard), acceptance bit-exact.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from helpers import assert_close, assert_lse_close, dev, host64
+
+pytestmark = pytest.mark.gpu
+
+skg = pytest.importorskip("sparse_kv_attention_sink_amd")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    skg.load()
+
+
+def run_draft(case, *, n_sink=0, window=0, idx=None):
+    q, k, v = dev(case.q), dev(case.k), dev(case.v)
+    cl = dev(case.cache_len)
+    idx_t = None if idx is None else dev(idx.astype(np.int32))
+    out, lse = skg.spec_attn_draft_sparse(q, k, v, cl, n_sink=n_sink, window=window, idx=idx_t,
+                                          scale=case.scale)
+    torch.cuda.synchronize()
+    return host64(out), lse.cpu().numpy().astype(np.float64)
+
+
+def run_verify(case, vq, tk, tv, parents, pad=None, workspace=None):
+    q = dev(vq)
+    k, v = dev(case.k), dev(case.v)
+    cl = dev(case.cache_len)
+    out, lse, pos = skg.spec_attn_verify_tree(q, k, v, cl, dev(tk), dev(tv),
+                                              dev(parents.astype(np.int32)),
+                                              pad=None if pad is None else dev(pad),
+                                              scale=case.scale, workspace=workspace)
+    torch.cuda.synchronize()
+    return host64(out), lse.cpu().numpy().astype(np.float64), pos.cpu().numpy()
+
+
+def run_accept(a: synth.AcceptCase):
+    res = skg.spec_accept_greedy(dev(a.logits), dev(a.tokens), dev(a.parents), a.max_depth)
+    torch.cuda.synchronize()
+    return [r.cpu().numpy() for r in res]
+
+
+# ------------------------------------------------------------ tiny fp32 workload
+
+def test_tiny_f32_draft_window():
+    c = synth.config_tiny()
+    case = c["case"]
+    got, lse = run_draft(case, n_sink=c["n_sink"], window=c["window"])
+    ref, lse_ref = oracle.draft_attn_ref(case.q, case.k, case.v, case.cache_len, scale=case.scale,
+                                         n_sink=c["n_sink"], window=c["window"])
+    assert_close(got, ref, "f32", "tiny draft")
+    assert_lse_close(lse, lse_ref, 1e-5, "tiny draft lse")
+
+
+def test_tiny_f32_verify_binary_tree():
+    c = synth.config_tiny()
+    case, tree = c["case"], c["tree"]
+    got, lse, pos = run_verify(case, c["verify_q"], c["tree_k"], c["tree_v"], tree.parents)
+    ref, lse_ref = oracle.verify_attn_ref(c["verify_q"], case.k, case.v,
+                                          case.cache_len, c["tree_k"], c["tree_v"], tree.parents,
+                                          scale=case.scale)
+    assert_close(got, ref, "f32", "tiny verify")
+    assert_lse_close(lse, lse_ref, 1e-5, "tiny verify lse")
+    np.testing.assert_array_equal(pos, oracle.position_ids(case.cache_len, None, tree.parents))
+
+
+@pytest.mark.parametrize("trial", range(64))
+def test_tiny_accept_planted(trial):
+    tree = synth.heap_tree(2, 3)
+    a = synth.make_accept_case(synth.SEEDS[1] + trial, tree, 1, 1000)
+    lens, paths, bonus = run_accept(a)
+    rl, rp, rb = oracle.accept_ref(a.logits, a.tokens, a.parents, a.max_depth)
+    np.testing.assert_array_equal(lens, rl)
+    np.testing.assert_array_equal(paths, rp)
+    np.testing.assert_array_equal(bonus, rb)
+    assert lens[0] == a.expected_len[0] and bonus[0] == a.expected_bonus[0]
+
+
+# ------------------------------------------------------------ 4K workload
+
+def test_4k_draft_budget():
+    c = synth.config_4k()
+    case = c["case"]
+    got, lse = run_draft(case, idx=c["idx"])
+    ref, lse_ref = oracle.draft_attn_ref(case.q, case.k, case.v, case.cache_len, scale=case.scale,
+                                         idx=c["idx"])
+    assert_close(got, ref, "bf16", "4K draft")
+    assert_lse_close(lse, lse_ref, 1e-3, "4K draft lse")
+
+
+def test_4k_verify_chain():
+    c = synth.config_4k()
+    case, tree = c["case"], c["tree"]
+    got, lse, pos = run_verify(case, c["verify_q"], c["tree_k"], c["tree_v"], tree.parents)
+    ref, lse_ref = oracle.verify_attn_ref(c["verify_q"], case.k, case.v, case.cache_len,
+                                          c["tree_k"], c["tree_v"], tree.parents, scale=case.scale)
+    assert_close(got, ref, "bf16", "4K verify")
+    assert_lse_close(lse, lse_ref, 1e-3, "4K verify lse")
+    np.testing.assert_array_equal(pos, oracle.position_ids(case.cache_len, None, tree.parents))
+
+
+def test_4k_accept():
+    a = synth.make_accept_case(synth.SEEDS[2] + 7, synth.chain_tree(5), 1, 128256)
+    got = run_accept(a)
+    for g, r in zip(got, oracle.accept_ref(a.logits, a.tokens, a.parents, a.max_depth)):
+        np.testing.assert_array_equal(g, r)
+
+
+# ------------------------------------------------------------ 16K workload
+
+@pytest.fixture(scope="module")
+def c16k():
+    return synth.config_16k()
+
+
+@pytest.mark.parametrize("budget", [256, 512, 1024, 2048])
+def test_16k_draft_budget_sweep(c16k, budget):
+    case = c16k["case"]
+    idx = c16k["idx"][budget]
+    got, lse = run_draft(case, idx=idx)
+    ref, lse_ref = oracle.draft_attn_ref(case.q, case.k, case.v, case.cache_len, scale=case.scale,
+                                         idx=idx)
+    assert_close(got, ref, "bf16", f"16K draft B={budget}")
+    assert_lse_close(lse, lse_ref, 1e-3, "16K draft lse")
+
+
+def test_16k_verify_64_node_tree_sampled(c16k):
+    """Full-size launch; the oracle checks every row of three (sequence,
+    KV head) pairs."""
+    case, tree = c16k["case"], c16k["tree"]
+    got, lse, pos = run_verify(case, c16k["verify_q"], c16k["tree_k"], c16k["tree_v"], tree.parents)
+    pairs = [(0, 0), (3, 5), (7, 7)]
+    ref, lse_ref = oracle.verify_attn_ref(c16k["verify_q"], case.k, case.v, case.cache_len,
+                                          c16k["tree_k"], c16k["tree_v"], tree.parents,
+                                          scale=case.scale, pairs=pairs)
+    assert_close(got, ref, "bf16", "16K verify")
+    assert_lse_close(lse, lse_ref, 1e-3, "16K verify lse")
+    assert np.all(np.isfinite(got))
+    np.testing.assert_array_equal(pos, oracle.position_ids(case.cache_len, None, tree.parents))
+
+
+def test_16k_accept(c16k):
+    a = synth.make_accept_case(synth.SEEDS[3] + 1, c16k["tree"], 8, 128256)
+    got = run_accept(a)
+    ref = oracle.accept_ref(a.logits, a.tokens, a.parents, a.max_depth)
+    for g, r in zip(got, ref):
+        np.testing.assert_array_equal(g, r)
+    np.testing.assert_array_equal(got[0], a.expected_len)
+
+
+# ------------------------------------------------------------ small ragged shapes
+
+SHAPES = [
+    # (B, Hq, Hkv, D, L_cap, lens, dtype)
+    (3, 4, 1, 64, 300, [1, 37, 300], "bf16"),
+    (2, 8, 2, 128, 517, [517, 203], "bf16"),
+    (2, 6, 2, 128, 97, [97, 5], "f32"),
+    (1, 8, 8, 64, 1000, [1000], "bf16"),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("T", [1, 3])
+@pytest.mark.parametrize("sink,win", [(4, 16), (0, 7), (5, 2000)])
+def test_ragged_draft_window(shape, T, sink, win):
+    B, Hq, Hkv, D, L, lens, dt = shape
+    lens = [max(x, T) for x in lens]
+    case = synth.make_attn_case(101 + T, B=B, Hq=Hq, Hkv=Hkv, D=D, L_cap=L, T=T, cache_len=lens,
+                                dtype=dt, value_scale=1.0)
+    got, lse = run_draft(case, n_sink=sink, window=win)
+    ref, lse_ref = oracle.draft_attn_ref(case.q, case.k, case.v, case.cache_len, scale=case.scale,
+                                         n_sink=sink, window=win)
+    assert_close(got, ref, dt, "ragged draft window")
+    assert_lse_close(lse, lse_ref, 1e-3 if dt == "bf16" else 1e-5, "ragged draft lse")
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("budget", [1, 33, 200])
+def test_ragged_draft_budget(shape, budget):
+    B, Hq, Hkv, D, L, lens, dt = shape
+    case = synth.make_attn_case(202 + budget, B=B, Hq=Hq, Hkv=Hkv, D=D, L_cap=L, T=1,
+                                cache_len=lens, dtype=dt, value_scale=1.0)
+    rng = np.random.default_rng(budget)
+    idx = np.stack([rng.integers(0, lens[b], size=(Hkv, budget)) for b in range(B)]).astype(np.int32)
+    got, lse = run_draft(case, idx=idx)
+    ref, lse_ref = oracle.draft_attn_ref(case.q, case.k, case.v, case.cache_len, scale=case.scale,
+                                         idx=idx)
+    assert_close(got, ref, dt, "ragged draft budget")
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("widths", [(1,), (3,), (1, 1, 1, 1, 1), (2, 4, 6), (10, 14, 12, 8)])
+def test_ragged_verify(shape, widths):
+    B, Hq, Hkv, D, L, lens, dt = shape
+    rng = np.random.default_rng(sum(widths) + D)
+    tree = synth.layered_tree(rng, widths)
+    N = tree.n
+    case = synth.make_attn_case(303 + N, B=B, Hq=Hq, Hkv=Hkv, D=D, L_cap=L, T=N, cache_len=lens,
+                                dtype=dt, value_scale=1.0)
+    tk = synth.draw_normal(rng, (B, Hkv, N, D), 1.0, dt)
+    tv = synth.draw_normal(rng, (B, Hkv, N, D), 1.0, dt)
+    pad = np.zeros((B, (L + 3) // 4 * 4), dtype=np.uint8)   # row stride: multiple of 4
+    for b in range(B):
+        pad[b, :lens[b]] = synth.pad_groups(rng, lens[b], n_groups=6, group=5)
+    got, lse, pos = run_verify(case, case.q, tk, tv, tree.parents, pad=pad)
+    ref, lse_ref = oracle.verify_attn_ref(case.q, case.k, case.v, case.cache_len, tk, tv,
+                                          tree.parents, scale=case.scale, pad=pad)
+    assert_close(got, ref, dt, "ragged verify")
+    assert_lse_close(lse, lse_ref, 1e-3 if dt == "bf16" else 1e-5, "ragged verify lse")
+    np.testing.assert_array_equal(pos, oracle.position_ids(case.cache_len, pad, tree.parents))
