@@ -117,8 +117,10 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
       anc = a.anc[(size_t)b * a.T + t];
     }
   }
+  // Splits are planned over the cache capacity; in verify mode the last split
+  // also takes the N tree keys that follow the cache positions.
   const int p0 = s * a.chunk;
-  const int p1 = min(n_keys, p0 + a.chunk);
+  const int p1 = (MODE == kVerify && s == a.splits - 1) ? n_keys : min(n_keys, p0 + a.chunk);
 
   float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
   bool idx_bad = false;
