@@ -1,0 +1,390 @@
+#!/usr/bin/env python3
+"""Benchmark of the speculative-decoding attention hot path on one MI355X.
+
+Headline workload: the million-token windowed-draft decode step.  One
+sequence with 1,048,576 cached tokens and 32 layers of bf16 KV (8 KV heads x
+head_dim 128, 128 GiB resident in HBM).  Per layer: verify attention of a
+3-token chain over the full cache, one draft "context" call (3 chained
+queries) and 3 single-query draft calls over sink 4 + window 4096; then one
+greedy acceptance over a 128256-token vocabulary.  The step time decomposes
+as t_verify + t_ctx_draft + 3 t_fwd_draft (per layer) + t_accept.
+
+Reported: algorithmic KV bytes per step / step time (GB/s, against the 8 TB/s
+HBM peak), steps per second, the per-component times, the roofline position
+of the dominant kernel (verify) measured with HIP events on the launch
+stream, the 16K-context batch-8 step per draft budget, and the fp64 CPU
+oracle timed on a bounded sample of the same workload.
+
+Inputs are seeded synthetic draws (no datasets, no weights); everything is
+resident on the GPU before the timed region starts.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "KV-attn HBM GB/s (% of peak) + draft+verify steps/sec, 16K and 1M ctx, 1 GPU"
+HBM_PEAK_GBS = 8000.0
+L1M, LAYERS, HQ, HKV, D, CHAIN, VOCAB = 1 << 20, 32, 32, 8, 128, 3, 128256
+SINK, WINDOW = 4, 4096
+ESZ = 2
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------ algorithmic bytes
+
+def window_view_len(L, T, sink, window):
+    """Keys one KV head reads for T chained queries over sink + window: the
+    sink part plus the union of the T windows (each key read once)."""
+    s_len = min(sink, L)
+    w_start = min(max(sink, L - T + 1 - window, 0), L)
+    return s_len + (L - w_start)
+
+
+def draft_bytes(B, L, T, view):
+    kv = B * HKV * view * 2 * D * ESZ
+    q_out = 2 * B * T * HQ * D * ESZ + B * T * HQ * 4
+    return kv + q_out
+
+
+def verify_bytes(B, L_sum, N, pad=False):
+    kv = HKV * (L_sum + B * N) * 2 * D * ESZ
+    q_out = 2 * B * N * HQ * D * ESZ + B * N * HQ * 4 + B * N * 4
+    return kv + q_out + (L_sum if pad else 0)
+
+
+def accept_bytes(B, N, V):
+    return B * (N + 1) * V * 4 + B * N * 4 * 2
+
+
+# ------------------------------------------------------------ 1M workload
+
+def run_1m(args, torch, skg):
+    import synth.device_gen as dg
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    layers = []
+    for li in range(args.layers):
+        layers.append(dg.layer_1m(li, device=dev))
+        if li % 8 == 7:
+            torch.cuda.synchronize()
+            log(f"[bench] generated layer {li + 1}/{args.layers} ({time.time() - t0:.1f}s)")
+    torch.cuda.synchronize()
+    log(f"[bench] generated {args.layers} layers of 1M-token KV in {time.time() - t0:.1f}s")
+
+    cache_len = torch.tensor([L1M], dtype=torch.int32, device=dev)
+    parents = torch.tensor([-1, 0, 1], dtype=torch.int32, device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(synth_seed(4) + 999)
+    logits = torch.randn((1, CHAIN + 1, VOCAB), generator=g, device=dev, dtype=torch.float32)
+    tokens = torch.randint(0, VOCAB, (1, CHAIN), generator=g, device=dev, dtype=torch.int32)
+
+    dims = skg.make_dims(1, HQ, HKV, D, skg.SPEC_BF16)
+    ws_v = skg.new_workspace(skg.verify_workspace_bytes(dims, CHAIN, L1M), dev)
+    ws_c = skg.new_workspace(skg.draft_workspace_bytes(dims, CHAIN, SINK + WINDOW + CHAIN - 1), dev)
+    ws_f = skg.new_workspace(skg.draft_workspace_bytes(dims, 1, SINK + WINDOW), dev)
+    ws_a = skg.new_workspace(skg.accept_workspace_bytes(1, CHAIN, VOCAB), dev)
+    v_out = torch.empty((1, CHAIN, HQ, D), dtype=torch.bfloat16, device=dev)
+    v_lse = torch.empty((1, CHAIN, HQ), dtype=torch.float32, device=dev)
+    v_pos = torch.empty((1, CHAIN), dtype=torch.int32, device=dev)
+    c_out = torch.empty_like(v_out)
+    c_lse = torch.empty_like(v_lse)
+    f_out = torch.empty((1, 1, HQ, D), dtype=torch.bfloat16, device=dev)
+    f_lse = torch.empty((1, 1, HQ), dtype=torch.float32, device=dev)
+    acc = [torch.empty(1, dtype=torch.int32, device=dev),
+           torch.empty((1, CHAIN), dtype=torch.int32, device=dev),
+           torch.empty(1, dtype=torch.int32, device=dev)]
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def step(marks=None):
+        for li, lay in enumerate(layers):
+            e = marks[li] if marks else None
+            if e: e[0].record()
+            skg.spec_attn_verify_tree(lay["verify_q"], lay["k"], lay["v"], cache_len,
+                                      lay["tree_k"], lay["tree_v"], parents, out=v_out, lse=v_lse,
+                                      pos_ids=v_pos, workspace=ws_v)
+            if e: e[1].record()
+            skg.spec_attn_draft_sparse(lay["ctx_q"], lay["k"], lay["v"], cache_len, n_sink=SINK,
+                                       window=WINDOW, out=c_out, lse=c_lse, workspace=ws_c)
+            if e: e[2].record()
+            for fq in lay["fwd_q"]:
+                skg.spec_attn_draft_sparse(fq, lay["k"], lay["v"], cache_len, n_sink=SINK,
+                                           window=WINDOW, out=f_out, lse=f_lse, workspace=ws_f)
+            if e: e[3].record()
+        skg.spec_accept_greedy(logits, tokens, parents, CHAIN, accept_len=acc[0],
+                               accept_path=acc[1], bonus=acc[2], workspace=ws_a)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    for w in (ws_v, ws_c, ws_f, ws_a):
+        assert skg.spec_device_status(w) == 0, "device range error during warmup"
+
+    marks = [[[ev() for _ in range(4)] for _ in layers] for _ in range(args.steps)]
+    start, stop = ev(), ev()
+    torch.cuda.synchronize()
+    start.record()
+    t_wall = time.perf_counter()
+    for k in range(args.steps):
+        step(marks[k])
+    stop.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_total = start.elapsed_time(stop)
+    ms_step = ms_total / args.steps
+
+    t_verify = [m[0].elapsed_time(m[1]) for st in marks for m in st]
+    t_ctx = [m[1].elapsed_time(m[2]) for st in marks for m in st]
+    t_fwd = [m[2].elapsed_time(m[3]) / CHAIN for st in marks for m in st]
+    n = args.layers
+    per_step_verify = sum(t_verify) / args.steps
+    per_step_ctx = sum(t_ctx) / args.steps
+    per_step_fwd = sum(t_fwd) * CHAIN / args.steps
+    t_acc = max(ms_step - per_step_verify - per_step_ctx - per_step_fwd, 0.0)
+
+    vb = verify_bytes(1, L1M, CHAIN)
+    cb = draft_bytes(1, L1M, CHAIN, window_view_len(L1M, CHAIN, SINK, WINDOW))
+    fb = draft_bytes(1, L1M, 1, window_view_len(L1M, 1, SINK, WINDOW))
+    ab = accept_bytes(1, CHAIN, VOCAB)
+    step_bytes = n * (vb + cb + CHAIN * fb) + ab
+    gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    v_avg_ms = sum(t_verify) / len(t_verify)
+    v_gbs = vb / (v_avg_ms * 1e-3) / 1e9
+    ctx_gbs = cb / (sum(t_ctx) / len(t_ctx) * 1e-3) / 1e9
+    fwd_gbs = fb / (sum(t_fwd) / len(t_fwd) * 1e-3) / 1e9
+    res = dict(
+        ms_step=ms_step, gbs=gbs, steps_per_s=1e3 / ms_step, step_bytes=step_bytes,
+        wall_ms_per_step=t_wall * 1e3 / args.steps,
+        components_ms=dict(t_verify=per_step_verify, t_ctx_draft=per_step_ctx,
+                           t_fwd_draft=per_step_fwd, t_accept_and_gaps=t_acc,
+                           verify_per_layer=v_avg_ms,
+                           ctx_draft_per_call=sum(t_ctx) / len(t_ctx),
+                           fwd_draft_per_call=sum(t_fwd) / len(t_fwd)),
+        call_gbs=dict(verify=v_gbs, ctx_draft=ctx_gbs, fwd_draft=fwd_gbs),
+        verify_bytes_per_launch=vb, verify_avg_ms=v_avg_ms,
+    )
+    return res, layers
+
+
+def synth_seed(c):
+    import synth
+    return synth.SEEDS[c]
+
+
+# ------------------------------------------------------------ 16K workload
+
+def run_16k(args, torch, skg):
+    """Batch 8 x 16K context; per draft budget B: t_verify(64-node tree) +
+    4 t_draft(B) + t_accept.  The KV is rotated over 16 copies (8 GiB) so
+    the 256 MB Infinity Cache does not serve the timed reads."""
+    import numpy as np
+    import synth
+    dev = torch.device("cuda:0")
+    Bsz, L, ROT = 8, 16384, 16
+    s = 1.0 / math.sqrt(D)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(synth.SEEDS[3] + 500)
+    kvs = []
+    for _ in range(ROT):
+        k = (torch.randn((Bsz, HKV, L, D), generator=gen, device=dev) * s).to(torch.bfloat16)
+        v = (torch.randn((Bsz, HKV, L, D), generator=gen, device=dev) * s).to(torch.bfloat16)
+        kvs.append((k, v))
+    tree = synth.layered_tree(np.random.default_rng(synth.SEEDS[3]), (10, 18, 18, 18))
+    N = tree.n
+    parents = torch.from_numpy(tree.parents).to(dev)
+    vq = (torch.randn((Bsz, N, HQ, D), generator=gen, device=dev) * s).to(torch.bfloat16)
+    tk = (torch.randn((Bsz, HKV, N, D), generator=gen, device=dev) * s).to(torch.bfloat16)
+    tv = (torch.randn((Bsz, HKV, N, D), generator=gen, device=dev) * s).to(torch.bfloat16)
+    dq = (torch.randn((Bsz, 1, HQ, D), generator=gen, device=dev) * s).to(torch.bfloat16)
+    cache_len = torch.full((Bsz,), L, dtype=torch.int32, device=dev)
+    logits = torch.randn((Bsz, N + 1, VOCAB), generator=gen, device=dev)
+    tokens = torch.randint(0, VOCAB, (Bsz, N), generator=gen, device=dev, dtype=torch.int32)
+    rng = np.random.default_rng(synth.SEEDS[3] + 1)
+    dims = skg.make_dims(Bsz, HQ, HKV, D, skg.SPEC_BF16)
+    ws_v = skg.new_workspace(skg.verify_workspace_bytes(dims, N, L), dev)
+    ws_a = skg.new_workspace(skg.accept_workspace_bytes(Bsz, N, VOCAB), dev)
+    out = {}
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    reps = max(args.steps, 4)
+    for bud in (256, 512, 1024, 2048):
+        idx = torch.from_numpy(np.stack([synth.budget_indices(rng, L, bud) for _ in range(Bsz)])
+                               [:, None, :]).to(dev)
+        ws_d = skg.new_workspace(skg.draft_workspace_bytes(dims, 1, bud), dev)
+
+        def step(i, marks=None):
+            k, v = kvs[i % ROT]
+            if marks: marks[0].record()
+            skg.spec_attn_verify_tree(vq, k, v, cache_len, tk, tv, parents, workspace=ws_v)
+            if marks: marks[1].record()
+            for j in range(4):
+                k2, v2 = kvs[(i + 1 + j) % ROT]
+                skg.spec_attn_draft_sparse(dq, k2, v2, cache_len, idx=idx, workspace=ws_d)
+            if marks: marks[2].record()
+            skg.spec_accept_greedy(logits, tokens, parents, 4, workspace=ws_a)
+            if marks: marks[3].record()
+
+        for i in range(2):
+            step(i)
+        torch.cuda.synchronize()
+        marks = [[ev() for _ in range(4)] for _ in range(reps * ROT // 4)]
+        a, b = ev(), ev()
+        a.record()
+        for i, m in enumerate(marks):
+            step(i * 5, m)
+        b.record()
+        torch.cuda.synchronize()
+        ms_step = a.elapsed_time(b) / len(marks)
+        tv_ms = sum(m[0].elapsed_time(m[1]) for m in marks) / len(marks)
+        td_ms = sum(m[1].elapsed_time(m[2]) for m in marks) / len(marks) / 4
+        ta_ms = sum(m[2].elapsed_time(m[3]) for m in marks) / len(marks)
+        vb = verify_bytes(Bsz, Bsz * L, N)
+        db = draft_bytes(Bsz, L, 1, bud) + Bsz * bud * 4
+        ab = accept_bytes(Bsz, N, VOCAB)
+        out[str(bud)] = dict(
+            ms_step=ms_step, steps_per_s=1e3 / ms_step,
+            gbs=(vb + 4 * db + ab) / (ms_step * 1e-3) / 1e9,
+            t_verify_ms=tv_ms, t_draft_ms=td_ms, t_accept_ms=ta_ms,
+            verify_gbs=vb / (tv_ms * 1e-3) / 1e9, draft_gbs=db / (td_ms * 1e-3) / 1e9,
+            accept_gbs=ab / (ta_ms * 1e-3) / 1e9,
+            verify_tflops=4 * D * HQ * N * Bsz * L / (tv_ms * 1e-3) / 1e12,
+        )
+    for w in (ws_v, ws_a):
+        assert skg.spec_device_status(w) == 0
+    del kvs
+    torch.cuda.empty_cache()
+    return out
+
+
+# ------------------------------------------------------------ CPU baseline
+
+def cpu_baseline(layers, torch, budget_s=12.0):
+    """The fp64 oracle on a bounded sample of the 1M step: for layer 0, one KV
+    head at a time, the verify of the 3-token chain over all 1,048,576 keys
+    plus the context and single-query draft calls of that head's 4 query
+    heads, until the time budget is spent."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    lay = layers[0]
+    G = HQ // HKV
+
+    def bits(t):
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+    vq, tkk, tvv, cq = (bits(lay[n]) for n in ("verify_q", "tree_k", "tree_v", "ctx_q"))
+    fq = [bits(x) for x in lay["fwd_q"]]
+    par = np.array([-1, 0, 1], dtype=np.int32)
+    cl = np.array([L1M], dtype=np.int32)
+    done_bytes, heads = 0, 0
+    t0 = time.perf_counter()
+    elapsed = 0.0
+    for g in range(HKV):
+        kb = bits(lay["k"][:, g:g + 1])
+        vb = bits(lay["v"][:, g:g + 1])
+        t1 = time.perf_counter()
+        hs = slice(g * G, (g + 1) * G)
+        oracle.verify_attn_ref(vq[:, :, hs], kb, vb, cl, tkk[:, g:g + 1], tvv[:, g:g + 1], par,
+                               scale=1 / math.sqrt(D))
+        oracle.draft_attn_ref(cq[:, :, hs], kb, vb, cl, scale=1 / math.sqrt(D), n_sink=SINK,
+                              window=WINDOW)
+        for f in fq:
+            oracle.draft_attn_ref(f[:, :, hs], kb, vb, cl, scale=1 / math.sqrt(D), n_sink=SINK,
+                                  window=WINDOW)
+        elapsed += time.perf_counter() - t1
+        heads += 1
+        done_bytes += (verify_bytes(1, L1M, CHAIN)
+                       + draft_bytes(1, L1M, CHAIN, window_view_len(L1M, CHAIN, SINK, WINDOW))
+                       + CHAIN * draft_bytes(1, L1M, 1, window_view_len(L1M, 1, SINK, WINDOW))) / HKV
+        if elapsed >= budget_s:
+            break
+    return dict(value=done_bytes / elapsed / 1e9, unit="GB/s", cores=threads, kind="oracle",
+                sample=f"1M step, layer 0, {heads} of 8 KV heads: chain-3 verify over 1,048,576 "
+                       f"keys + 1 context and 3 single-query window draft calls per head "
+                       f"(fp64 NumPy oracle, {elapsed:.1f}s; host cores visible: {os.cpu_count()})",
+                seconds=elapsed)
+
+
+# ------------------------------------------------------------ main
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--layers", type=int, default=LAYERS)
+    ap.add_argument("--skip-16k", action="store_true")
+    ap.add_argument("--skip-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only: the hot path needs no "
+                                   "collectives, and --gpus above 1 is not supported"}))
+        sys.exit(2)
+    import torch
+    import sparse_kv_attention_sink_amd as skg
+    skg.load()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    r1m, layers = run_1m(args, torch, skg)
+    log(f"[bench] 1M step: {r1m['ms_step']:.3f} ms, {r1m['gbs']:.1f} GB/s")
+    cpu = None
+    if not args.skip_cpu:
+        cpu = cpu_baseline(layers, torch)
+        log(f"[bench] cpu oracle: {cpu['value']:.3f} GB/s")
+    del layers
+    torch.cuda.empty_cache()
+    r16 = None if args.skip_16k else run_16k(args, torch, skg)
+
+    v_ms = r1m["verify_avg_ms"]
+    achieved = r1m["verify_bytes_per_launch"] / (v_ms * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(r1m["gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r1m["ms_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1)/sqrt(128) bf16 KV and queries drawn on the GPU "
+                "(no datasets, no trained weights)",
+        "config": {"workload": "1M-token windowed draft + chain-3 verify step",
+                   "batch": 1, "context": L1M, "layers": args.layers, "q_heads": HQ,
+                   "kv_heads": HKV, "head_dim": D, "draft": "sink 4 + window 4096; per layer "
+                   "1 context call (3 chained queries) + 3 single-query calls",
+                   "verify": "3-token chain over the full cache per layer", "vocab": VOCAB},
+        "pct_of_hbm_peak": round(100 * r1m["gbs"] / HBM_PEAK_GBS, 2),
+        "steps_per_s": round(r1m["steps_per_s"], 3),
+        "components_ms": {k: round(v, 4) for k, v in r1m["components_ms"].items()},
+        "call_gbs": {k: round(v, 1) for k, v in r1m["call_gbs"].items()},
+        "roofline": {"kernel": "verify (chain 3 over 1,048,576 keys, 8 KV heads)",
+                     "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": r1m["verify_bytes_per_launch"],
+                     "avg_launch_ms": round(v_ms, 4)},
+        "cpu_baseline": cpu,
+        "ctx16k": r16,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
