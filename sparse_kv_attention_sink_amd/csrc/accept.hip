@@ -37,6 +37,15 @@ __device__ __forceinline__ void arg_consider(float& bv, int& bi, float v, int i)
   }
 }
 
+// Within one thread indices only increase, so a strict ">" keeps the first
+// maximum and a NaN, once held, is never replaced; the full rule (with index
+// tie-breaks) is only needed when merging across threads.
+__device__ __forceinline__ void scan_one(float& bv, int& bi, float v, int i) {
+  const bool take = v > bv || (isnan(v) && !isnan(bv));
+  bv = take ? v : bv;
+  bi = take ? i : bi;
+}
+
 __global__ __launch_bounds__(256) void argmax_partial_kernel(const float* __restrict__ logits,
                                                              int64_t V, int vsplits, int64_t vchunk,
                                                              ArgBest* __restrict__ part) {
@@ -47,21 +56,40 @@ __global__ __launch_bounds__(256) void argmax_partial_kernel(const float* __rest
   const int64_t v1 = min(V, v0 + vchunk);
   float bv = -INFINITY;
   int bi = INT_MAX;
-  // unaligned head, 16-byte body, tail
+  // unaligned head, 16-byte body (4 loads in flight per thread), tail
   int64_t a0 = v0;
   const int64_t mis = (reinterpret_cast<uintptr_t>(x + v0) >> 2) & 3;
   if (mis) a0 = min(v1, v0 + (4 - mis));
   for (int64_t v = v0 + tid; v < a0; v += 256) arg_consider(bv, bi, x[v], (int)v);
   const int64_t nvec = (v1 - a0) / 4;
   const float4* xv = reinterpret_cast<const float4*>(x + a0);
-  for (int64_t k = tid; k < nvec; k += 256) {
+  // thread-local results are merged with arg_consider, so each thread may scan
+  // its own index sequence in increasing order
+  float tv = -INFINITY;
+  int ti = INT_MAX;
+  int64_t k = tid;
+  for (; k + 3 * 256 < nvec; k += 4 * 256) {
+    float4 f[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) f[u] = load_stream_f4(xv + k + u * 256);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int base = (int)(a0 + 4 * (k + u * 256));
+      scan_one(tv, ti, f[u].x, base);
+      scan_one(tv, ti, f[u].y, base + 1);
+      scan_one(tv, ti, f[u].z, base + 2);
+      scan_one(tv, ti, f[u].w, base + 3);
+    }
+  }
+  for (; k < nvec; k += 256) {
     const float4 f = xv[k];
     const int base = (int)(a0 + 4 * k);
-    arg_consider(bv, bi, f.x, base);
-    arg_consider(bv, bi, f.y, base + 1);
-    arg_consider(bv, bi, f.z, base + 2);
-    arg_consider(bv, bi, f.w, base + 3);
+    scan_one(tv, ti, f.x, base);
+    scan_one(tv, ti, f.y, base + 1);
+    scan_one(tv, ti, f.z, base + 2);
+    scan_one(tv, ti, f.w, base + 3);
   }
+  if (ti != INT_MAX) arg_consider(bv, bi, tv, ti);
   for (int64_t v = a0 + 4 * nvec + tid; v < v1; v += 256) arg_consider(bv, bi, x[v], (int)v);
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) {
@@ -82,6 +110,10 @@ __global__ __launch_bounds__(256) void argmax_partial_kernel(const float* __rest
   }
 }
 
+// One wavefront per sequence, lane i = node i: finish the argmax of every
+// row, then accepted(i) = every node on i's root path carries its parent's
+// greedy target (ancestor masks by walking parents), and the result is the
+// deepest accepted node, ties to the smallest index.
 __global__ __launch_bounds__(64) void accept_walk_kernel(
     int N, int vsplits, const ArgBest* __restrict__ part, const int32_t* __restrict__ tokens,
     const int32_t* __restrict__ parents, int64_t par_sb, int max_depth, int32_t* accept_len,
@@ -97,47 +129,50 @@ __global__ __launch_bounds__(64) void accept_walk_kernel(
     am[r] = bi;
   }
   bool bad = false;
+  int pr = -1, tok = 0;
   if (lane < N) {
-    const int pr = parents[b * par_sb + lane];
+    pr = parents[b * par_sb + lane];
+    tok = tokens[(int64_t)b * N + lane];
     par_s[lane] = pr;
     bad = !(pr >= -1 && pr < lane);
   }
   const bool any_bad = __syncthreads_or(bad);
-  if (lane != 0) return;
   int32_t* path = accept_path + (int64_t)b * max_depth;
   if (any_bad) {
-    raise_error(err, SPEC_DEV_PARENT);
-    accept_len[b] = -1;
-    bonus[b] = -1;
-    for (int k = 0; k < max_depth; ++k) path[k] = -1;
+    if (lane == 0) {
+      raise_error(err, SPEC_DEV_PARENT);
+      accept_len[b] = -1;
+      bonus[b] = -1;
+    }
+    for (int k = lane; k < max_depth; k += 64) path[k] = -1;
     return;
   }
-  // accepted flags and depths in node order; keep the deepest accepted node
-  uint64_t acc = 0;
-  int depth[kMaxNodes];
-  int best = -1, best_depth = -1;
-  for (int i = 0; i < N; ++i) {
-    const int pr = par_s[i];
-    depth[i] = pr < 0 ? 0 : depth[pr] + 1;
-    const bool parent_ok = pr < 0 || ((acc >> pr) & 1ull);
-    if (parent_ok && tokens[(int64_t)b * N + i] == am[pr + 1]) {
-      acc |= 1ull << i;
-      if (depth[i] > best_depth) {
-        best = i;
-        best_depth = depth[i];
-      }
+  const bool match = lane < N && tok == am[pr + 1];
+  const uint64_t match_mask = __ballot(match);
+  uint64_t anc = 0;
+  int depth = -1;
+  if (lane < N)
+    for (int j = lane; j >= 0; j = par_s[j]) {
+      anc |= 1ull << j;
+      ++depth;
     }
+  const bool acc = lane < N && (anc & ~match_mask) == 0;
+  // deepest accepted node, ties to the smallest index
+  int key = acc ? (depth << 8) | (255 - lane) : -1;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) key = max(key, __shfl_xor(key, m, 64));
+  const int best = key < 0 ? -1 : 255 - (key & 255);
+  const int len = key < 0 ? 0 : (key >> 8) + 1;
+  const uint64_t best_anc = best < 0 ? 0ull : __shfl(anc, best, 64);
+  __shared__ int on_path[kMaxNodes];
+  if (lane < N && ((best_anc >> lane) & 1ull)) on_path[depth] = lane;
+  __syncthreads();
+  for (int k = lane; k < max_depth; k += 64) path[k] = k < len ? on_path[k] : -1;
+  if (lane == 0) {
+    if (len > max_depth) raise_error(err, SPEC_DEV_DEPTH);
+    accept_len[b] = len;
+    bonus[b] = am[best + 1];
   }
-  const int len = best < 0 ? 0 : best_depth + 1;
-  for (int k = 0; k < max_depth; ++k) path[k] = -1;
-  int j = best;
-  for (int k = len - 1; k >= 0; --k) {
-    if (k < max_depth) path[k] = j;
-    j = par_s[j];
-  }
-  if (len > max_depth) raise_error(err, SPEC_DEV_DEPTH);
-  accept_len[b] = len;
-  bonus[b] = am[best + 1];
 }
 
 hipError_t launch_accept(int B, int N, int V, const float* logits, const int32_t* tokens,

@@ -41,6 +41,8 @@ spec_status hip_fail(hipError_t e, const char* what) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+int64_t esize(int dtype) { return dtype == SPEC_BF16 ? 2 : 4; }
+
 constexpr int64_t kTargetWaves = 2048;     // 256 CUs x 8 wavefronts
 constexpr int64_t kMaxGrid = 0x7fffffff;
 
@@ -60,8 +62,6 @@ spec_status check_dims(const spec_dims* d) {
   return SPEC_OK;
 }
 
-size_t esize(int dtype) { return dtype == SPEC_BF16 ? 2 : 4; }
-
 spec_status check_kv(const spec_kv* kv, const spec_dims* d, const char* name, bool need_cap) {
   if (kv == nullptr) return fail(SPEC_E_INVALID, "%s is NULL", name);
   if (kv->k == nullptr || kv->v == nullptr) return fail(SPEC_E_INVALID, "%s.k / %s.v is NULL", name, name);
@@ -74,6 +74,9 @@ spec_status check_kv(const spec_kv* kv, const spec_dims* d, const char* name, bo
   if (kv->stride_b % m || kv->stride_h % m || kv->stride_t % m)
     return fail(SPEC_E_INVALID, "%s strides must be multiples of %lld elements", name, (long long)m);
   if (need_cap && kv->capacity < 0) return fail(SPEC_E_INVALID, "%s.capacity %d < 0", name, kv->capacity);
+  // kernels address a 32-token tile with 32-bit byte offsets
+  if (kv->stride_t * (int64_t)esize(d->dtype) * 64 > INT32_MAX)
+    return fail(SPEC_E_UNSUPPORTED, "%s.stride_t %lld is too large", name, (long long)kv->stride_t);
   return SPEC_OK;
 }
 

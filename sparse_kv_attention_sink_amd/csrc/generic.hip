@@ -14,52 +14,76 @@
 
 namespace spec {
 
-__global__ __launch_bounds__(128) void combine_kernel(AttnArgs a, int dtype) {
+// One block per (pair, row): 256 threads; thread (d, g) sums the splits
+// s = g, g + 256/D, ... for head-dim element d; empty splits hold o = 0 and
+// x = -inf, so their weight 2^(x - M) is exactly 0 and no branch is needed.
+__global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int dtype) {
   const int row = blockIdx.x % a.R;
   const int pair = blockIdx.x / a.R;
   const int z = row / a.rb, i = row % a.rb;
-  const int d = threadIdx.x;
-  const size_t base = (((size_t)pair * a.n_rb + z) * a.splits) * a.rb + i;
+  const int tid = threadIdx.x;
+  const int S = a.splits, D = a.D;
+  const size_t base = (((size_t)pair * a.n_rb + z) * S) * a.rb + i;
+  __shared__ float s_max[4];
+  __shared__ float s_o[256], s_w[256];
+
   float M = -INFINITY;
   bool nan = false;
-  for (int s = 0; s < a.splits; ++s) {
+  for (int s = tid; s < S; s += 256) {
     const float x = a.lse_part[base + (size_t)s * a.rb];
     nan |= isnan(x);
     M = fmaxf(M, x);
   }
-  float o = 0.f, wsum = 0.f;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
+  if ((tid & 63) == 0) s_max[tid >> 6] = M;
+  nan = __syncthreads_or(nan);
+  M = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+
+  const int groups = 256 / D;
+  const int d = tid % D, grp = tid / D;
+  float o = 0.f, w = 0.f;
   if (!nan && M != -INFINITY) {
-    for (int s = 0; s < a.splits; ++s) {
+#pragma unroll 4
+    for (int s = grp; s < S; s += groups) {
       const size_t ps = base + (size_t)s * a.rb;
-      const float x = a.lse_part[ps];
-      if (x == -INFINITY) continue;
-      const float w = exp2f(x - M);
-      wsum += w;
-      o += w * a.o_part[ps * a.D + d];
+      const float ws = __builtin_amdgcn_exp2f(a.lse_part[ps] - M);
+      w += ws;
+      o += ws * a.o_part[ps * D + d];
     }
-    o /= wsum;
   }
-  float lse2 = M + log2f(wsum);
+  s_o[tid] = o;
+  s_w[tid] = w;
+  __syncthreads();
+  if (grp != 0) return;
+  for (int g2 = 1; g2 < groups; ++g2) {
+    o += s_o[g2 * D + d];
+    w += s_w[g2 * D + d];
+  }
+  float lse2;
   if (nan) {
     o = NAN;
     lse2 = NAN;
   } else if (M == -INFINITY) {
     o = 0.f;
     lse2 = -INFINITY;
+  } else {
+    o /= w;
+    lse2 = M + log2f(w);
   }
   const int b = pair / a.Hkv, g = pair % a.Hkv;
   const int t = row / a.G, hh = row % a.G;
   const size_t oi = (((size_t)b * a.T + t) * a.Hq + g * a.G + hh);
   if (dtype == SPEC_BF16)
-    reinterpret_cast<uint16_t*>(a.out)[oi * a.D + d] = (uint16_t)f32_to_bf16(o);
+    reinterpret_cast<uint16_t*>(a.out)[oi * D + d] = (uint16_t)f32_to_bf16(o);
   else
-    reinterpret_cast<float*>(a.out)[oi * a.D + d] = o;
+    reinterpret_cast<float*>(a.out)[oi * D + d] = o;
   if (d == 0 && a.lse != nullptr) a.lse[oi] = lse2 * kLn2;
 }
 
 hipError_t launch_combine(const AttnArgs& a, int dtype, hipStream_t st) {
   const int64_t blocks = (int64_t)a.B * a.Hkv * a.R;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(a.D), 0, st, a, dtype);
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a, dtype);
   return hipGetLastError();
 }
 

@@ -61,20 +61,103 @@ __global__ __launch_bounds__(256) void verify_prep_kernel(
   if ((tid & 63) == 0) cnt_s[tid >> 6] = cnt;
   __syncthreads();
 
+  const int n_pad = cnt_s[0] + cnt_s[1] + cnt_s[2] + cnt_s[3];
+  const bool bad = bad_len || any_bad_par;
   if (tid == 0) {
-    const int n_pad = cnt_s[0] + cnt_s[1] + cnt_s[2] + cnt_s[3];
-    const bool bad = bad_len || any_bad_par;
     if (bad_len) raise_error(err, SPEC_DEV_CACHE_LEN);
     if (any_bad_par) raise_error(err, SPEC_DEV_PARENT);
     bad_ws[b] = bad ? 1 : 0;
-    uint64_t anc[kMaxNodes];
-    int depth[kMaxNodes];
-    for (int i = 0; i < N; ++i) {
-      const int p = bad ? -1 : par_s[i];
-      anc[i] = (p < 0 ? 0ull : anc[p]) | (1ull << i);
-      depth[i] = p < 0 ? 0 : depth[p] + 1;
-      anc_ws[(size_t)b * N + i] = bad ? 0ull : anc[i];
-      if (pos_ids != nullptr) pos_ids[(size_t)b * N + i] = bad ? -1 : (L - n_pad) + depth[i];
+  }
+  if (tid < N) {
+    // walk to the root: parents precede children, so this ends
+    uint64_t anc = 0;
+    int depth = -1;
+    if (!bad) {
+      for (int j = tid; j >= 0; j = par_s[j]) {
+        anc |= 1ull << j;
+        ++depth;
+      }
+    }
+    anc_ws[(size_t)b * N + tid] = anc;
+    if (pos_ids != nullptr) pos_ids[(size_t)b * N + tid] = bad ? -1 : (L - n_pad) + depth;
+  }
+}
+
+// ------------------------------------------------------------------ tile staging
+
+__device__ __forceinline__ uint32_t u4get(const uint4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// Issue the global loads of one 32-key tile (K rows natural, V rows in groups
+// of 4 keys x 8 head-dim elements per lane).  Addresses are a wave-uniform
+// tile base plus per-lane 32-bit byte offsets; keys at or past `limit` (only
+// in a split's last, partial tile) re-read the last valid row, and their
+// scores are masked.
+template <int D>
+__device__ __forceinline__ void load_tile(uint4 (&kreg)[(32 * D / 8) / 64], uint4 (&vreg)[D / 8 / 8 * 4],
+                                          const uint16_t* kp, const uint16_t* vp, int64_t st,
+                                          int base, int limit, int lane) {
+  constexpr int LPR = D / 8, RPI = 64 / LPR, NIK = 32 / RPI, NU = LPR / 8;
+  const int row_in = lane / LPR, ch = lane % LPR;
+  const uint32_t stb = (uint32_t)st * 2u;                 // row stride in bytes
+  const char* kb = reinterpret_cast<const char*>(kp + (int64_t)base * st);
+  const char* vb = reinterpret_cast<const char*>(vp + (int64_t)base * st);
+  const uint32_t col = (uint32_t)ch * 16u;
+  if (base + 32 <= limit) {
+#pragma unroll
+    for (int j = 0; j < NIK; ++j)
+      kreg[j] = load_stream(kb + ((uint32_t)(j * RPI + row_in) * stb + col));
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int kg = lane / LPR + (64 / LPR) * u;
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        vreg[u * 4 + r4] = load_stream(vb + ((uint32_t)(kg * 4 + r4) * stb + col));
+    }
+  } else {
+    const int last = limit - 1 - base;
+#pragma unroll
+    for (int j = 0; j < NIK; ++j)
+      kreg[j] = load_stream(kb + ((uint32_t)min(j * RPI + row_in, last) * stb + col));
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int kg = lane / LPR + (64 / LPR) * u;
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        vreg[u * 4 + r4] = load_stream(vb + ((uint32_t)min(kg * 4 + r4, last) * stb + col));
+    }
+  }
+}
+
+// K rows go to a padded LDS tile; V goes transposed (head-dim major, 4-key
+// groups swizzled by head-dim block) so that the P.V operand of a lane (8
+// keys at one head-dim column) is two 8-byte LDS reads.
+template <int D>
+__device__ __forceinline__ void store_tile(uint8_t* k_lds, uint8_t* v_lds,
+                                           const uint4 (&kreg)[(32 * D / 8) / 64],
+                                           const uint4 (&vreg)[D / 8 / 8 * 4], int lane) {
+  constexpr int LPR = D / 8, RPI = 64 / LPR, NIK = 32 / RPI, NU = LPR / 8;
+  constexpr int KP = 2 * D + 16, VP = 72;
+  const int row_in = lane / LPR, ch = lane % LPR;
+#pragma unroll
+  for (int j = 0; j < NIK; ++j)
+    *reinterpret_cast<uint4*>(k_lds + (j * RPI + row_in) * KP + ch * 16) = kreg[j];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int kg = lane / LPR + (64 / LPR) * u;
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      // head-dim pair (2*e2, 2*e2+1) of keys kg*4 .. kg*4+3
+      const uint32_t a0 = u4get(vreg[u * 4 + 0], e2), a1 = u4get(vreg[u * 4 + 1], e2);
+      const uint32_t a2 = u4get(vreg[u * 4 + 2], e2), a3 = u4get(vreg[u * 4 + 3], e2);
+      const uint2 lo = make_uint2(__builtin_amdgcn_perm(a1, a0, 0x05040100u),
+                                  __builtin_amdgcn_perm(a3, a2, 0x05040100u));
+      const uint2 hi = make_uint2(__builtin_amdgcn_perm(a1, a0, 0x07060302u),
+                                  __builtin_amdgcn_perm(a3, a2, 0x07060302u));
+      const int d0 = ch * 8 + 2 * e2, d1 = d0 + 1;
+      *reinterpret_cast<uint2*>(v_lds + d0 * VP + ((kg ^ ((d0 >> 4) & 7)) * 8)) = lo;
+      *reinterpret_cast<uint2*>(v_lds + d1 * VP + ((kg ^ ((d1 >> 4) & 7)) * 8)) = hi;
     }
   }
 }
@@ -91,6 +174,7 @@ __global__ __launch_bounds__(64) void verify_mfma_kernel(AttnArgs a) {
   constexpr int RPI = 64 / LPR;         // key rows per load instruction
   constexpr int NIK = 32 / RPI;         // K load instructions per tile
   constexpr int NU = LPR / 8;           // V units (4 keys x 8 dims) per lane
+  (void)KP;
   __shared__ __attribute__((aligned(16))) uint8_t k_lds[32 * KP];
   __shared__ __attribute__((aligned(16))) uint8_t v_lds[D * VP];
 
@@ -149,33 +233,13 @@ __global__ __launch_bounds__(64) void verify_mfma_kernel(AttnArgs a) {
   const uint16_t* tvp = reinterpret_cast<const uint16_t*>(a.tv) + b * a.tkb + g * a.tkh;
   const uint8_t* padrow = a.pad ? a.pad + b * a.pad_sb : nullptr;
 
-  const int row_in = lane / LPR, ch = lane % LPR;
-  uint4 kreg[NIK], vreg[NU][4];
+  uint4 kreg[NIK], vreg[NU * 4];
 
-  auto load_tile = [&](int tile) {
-    const bool tree = tile >= n_cache_tiles;
-    const int base = tree ? (tile - n_cache_tiles) * 32 : c0 + tile * 32;
-    const int limit = tree ? N : c1;
-    const uint16_t* kp = tree ? tkp : kc;
-    const uint16_t* vp = tree ? tvp : vc;
-    const int64_t st = tree ? a.tkt : a.kt;
-#pragma unroll
-    for (int j = 0; j < NIK; ++j) {
-      const int key = min(base + j * RPI + row_in, limit - 1);
-      kreg[j] = *reinterpret_cast<const uint4*>(kp + key * st + ch * 8);
-    }
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      const int kg = lane / LPR + (64 / LPR) * u;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = min(base + kg * 4 + r, limit - 1);
-        vreg[u][r] = *reinterpret_cast<const uint4*>(vp + key * st + ch * 8);
-      }
-    }
-  };
-
-  if (n_tiles > 0) load_tile(0);
+  if (n_tiles > 0) {
+    const bool tree0 = n_cache_tiles == 0;
+    load_tile<D>(kreg, vreg, tree0 ? tkp : kc, tree0 ? tvp : vc, tree0 ? a.tkt : a.kt,
+                 tree0 ? 0 : c0, tree0 ? N : c1, lane);
+  }
 
   for (int tile = 0; tile < n_tiles; ++tile) {
     const bool tree = tile >= n_cache_tiles;
@@ -183,31 +247,14 @@ __global__ __launch_bounds__(64) void verify_mfma_kernel(AttnArgs a) {
     const int limit = tree ? N : c1;
 
     __syncthreads();   // previous tile's LDS reads are done
-#pragma unroll
-    for (int j = 0; j < NIK; ++j)
-      *reinterpret_cast<uint4*>(k_lds + (j * RPI + row_in) * KP + ch * 16) = kreg[j];
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      const int kg = lane / LPR + (64 / LPR) * u;
-      const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vreg[u][0]);
-      const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vreg[u][1]);
-      const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vreg[u][2]);
-      const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vreg[u][3]);
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        // head-dim pair (2*e2, 2*e2+1) of keys kg*4 .. kg*4+3
-        const uint32_t a0 = w0[e2], a1 = w1[e2], a2 = w2[e2], a3 = w3[e2];
-        const uint2 lo = make_uint2(__builtin_amdgcn_perm(a1, a0, 0x05040100u),
-                                    __builtin_amdgcn_perm(a3, a2, 0x05040100u));
-        const uint2 hi = make_uint2(__builtin_amdgcn_perm(a1, a0, 0x07060302u),
-                                    __builtin_amdgcn_perm(a3, a2, 0x07060302u));
-        const int d0 = ch * 8 + 2 * e2, d1 = d0 + 1;
-        *reinterpret_cast<uint2*>(v_lds + d0 * VP + ((kg ^ ((d0 >> 4) & 7)) * 8)) = lo;
-        *reinterpret_cast<uint2*>(v_lds + d1 * VP + ((kg ^ ((d1 >> 4) & 7)) * 8)) = hi;
-      }
-    }
+    store_tile<D>(k_lds, v_lds, kreg, vreg, lane);
     __syncthreads();
-    if (tile + 1 < n_tiles) load_tile(tile + 1);
+    if (tile + 1 < n_tiles) {
+      const bool ntree = tile + 1 >= n_cache_tiles;
+      const int nbase = ntree ? (tile + 1 - n_cache_tiles) * 32 : c0 + (tile + 1) * 32;
+      load_tile<D>(kreg, vreg, ntree ? tkp : kc, ntree ? tvp : vc, ntree ? a.tkt : a.kt, nbase,
+                   ntree ? N : c1, lane);
+    }
 
     // Visibility of this lane's 8 keys: base + h*16 + q4*4 + i.
     uint32_t padw[2] = {0u, 0u};
@@ -255,11 +302,11 @@ __global__ __launch_bounds__(64) void verify_mfma_kernel(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) p[e] = 0.f;
       } else {
-        const float alpha = exp2f(m[rt] - mn);
+        const float alpha = __builtin_amdgcn_exp2f(m[rt] - mn);
         float ps = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          p[e] = exp2f(t[e] - mn);
+          p[e] = __builtin_amdgcn_exp2f(t[e] - mn);
           ps += p[e];
         }
         lsum[rt] = lsum[rt] * alpha + ps;
