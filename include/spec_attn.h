@@ -29,13 +29,19 @@
  *     written as NaN (attention) or -1 (token outputs).  spec_device_status()
  *     reports and clears that word.
  *   - Workspace: a caller-allocated device buffer of at least the size the
- *     matching spec_*_workspace_bytes() returns, zero-filled once before its
- *     first use.  It may be reused by any later call issued to the same
- *     stream; calls that overlap in time (different streams) need separate
+ *     matching spec_*_workspace_bytes() returns, zero-filled before its first
+ *     use.  It holds arrival counters that every call leaves at zero again,
+ *     so it may be reused by any later call issued to the same stream as
+ *     long as the shape arguments are the same; after a call with other
+ *     shapes, zero it again (the counters sit at shape-dependent offsets).
+ *     Calls that overlap in time (different streams) need separate
  *     workspaces.  Sizes depend only on the arguments, never on the device.
  *   - dtype SPEC_BF16 is the tuned path (bf16 inputs, fp32 accumulation, bf16
  *     outputs rounded to nearest-even); SPEC_F32 is a plain fp32 path.
  *   - head_dim must be 64 or 128.  Query head h reads KV head h / (Hq / Hkv).
+ *   - Size limits of the bf16 path (SPEC_E_UNSUPPORTED beyond them): a
+ *     draft budget of at most 131072 positions; a verify cache capacity plus
+ *     N of at most 2^21 slots.
  *
  * Sources (page title, then the passage):
  *   [WM] "Windowed-MTP: Removing the Full-Context Draft-KV Tax at Million-Token

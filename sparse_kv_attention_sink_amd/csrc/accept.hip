@@ -8,12 +8,12 @@
 // for Long-Context Generation via Partial Verification", section 4.1
 // "Metrics": the accept length may be 0.
 //
-// Two kernels.  (1) Split-vocabulary argmax: each block scans a contiguous
-// slice of one logits row with 16-byte loads and reduces (value, index)
-// pairs by shuffles under the rule "larger value wins, NaN beats every
-// number, ties go to the smaller index"; the per-slice winners land in the
-// workspace.  (2) One wavefront per sequence finishes the argmax of every
-// row, then walks the tree in node order (parents precede children).
+// One kernel.  Each block scans a contiguous slice of one logits row with
+// 16-byte loads and reduces (value, index) pairs under the rule "larger value
+// wins, NaN beats every number, ties go to the smaller index"; the slice's
+// winner lands in the workspace.  The block that finishes a sequence's rows
+// last (arrival counter per sequence) finishes the argmax of every row and
+// walks the tree in node order (parents precede children).
 #include "dev_common.h"
 
 namespace spec {
@@ -38,25 +38,21 @@ __device__ __forceinline__ void arg_consider(float& bv, int& bi, float v, int i)
 }
 
 // Within one thread indices only increase, so a strict ">" keeps the first
-// maximum and a NaN, once held, is never replaced; the full rule (with index
-// tie-breaks) is only needed when merging across threads.
+// maximum and a NaN, once held, is never replaced; the first element is
+// always taken (a row of -inf still has an argmax).  The full rule (with
+// index tie-breaks) is only needed when merging across threads.
 __device__ __forceinline__ void scan_one(float& bv, int& bi, float v, int i) {
-  const bool take = v > bv || (isnan(v) && !isnan(bv));
+  const bool take = v > bv || (isnan(v) && !isnan(bv)) || bi == INT_MAX;
   bv = take ? v : bv;
   bi = take ? i : bi;
 }
 
-__global__ __launch_bounds__(256) void argmax_partial_kernel(const float* __restrict__ logits,
-                                                             int64_t V, int vsplits, int64_t vchunk,
-                                                             ArgBest* __restrict__ part) {
-  const int row = blockIdx.x / vsplits, sp = blockIdx.x % vsplits;
+// Argmax of one logits slice (all 256 threads); returns the winner in thread 0.
+__device__ ArgBest slice_argmax(const float* __restrict__ x, int64_t v0, int64_t v1) {
   const int tid = threadIdx.x;
-  const float* x = logits + (int64_t)row * V;
-  const int64_t v0 = (int64_t)sp * vchunk;
-  const int64_t v1 = min(V, v0 + vchunk);
   float bv = -INFINITY;
   int bi = INT_MAX;
-  // unaligned head, 16-byte body (4 loads in flight per thread), tail
+  // unaligned head, 16-byte body (8 loads in flight per thread), tail
   int64_t a0 = v0;
   const int64_t mis = (reinterpret_cast<uintptr_t>(x + v0) >> 2) & 3;
   if (mis) a0 = min(v1, v0 + (4 - mis));
@@ -68,12 +64,13 @@ __global__ __launch_bounds__(256) void argmax_partial_kernel(const float* __rest
   float tv = -INFINITY;
   int ti = INT_MAX;
   int64_t k = tid;
-  for (; k + 3 * 256 < nvec; k += 4 * 256) {
-    float4 f[4];
+  constexpr int U = 8;
+  for (; k + (U - 1) * 256 < nvec; k += U * 256) {
+    float4 f[U];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) f[u] = load_stream_f4(xv + k + u * 256);
+    for (int u = 0; u < U; ++u) f[u] = load_stream_f4(xv + k + u * 256);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < U; ++u) {
       const int base = (int)(a0 + 4 * (k + u * 256));
       scan_one(tv, ti, f[u].x, base);
       scan_one(tv, ti, f[u].y, base + 1);
@@ -104,90 +101,115 @@ __global__ __launch_bounds__(256) void argmax_partial_kernel(const float* __rest
     si[tid >> 6] = bi;
   }
   __syncthreads();
-  if (tid == 0) {
+  if (tid == 0)
     for (int w = 1; w < 4; ++w) arg_consider(bv, bi, sv[w], si[w]);
-    part[(int64_t)row * vsplits + sp] = ArgBest{bv, bi};
-  }
+  return ArgBest{bv, bi};
 }
 
-// One wavefront per sequence, lane i = node i: finish the argmax of every
-// row, then accepted(i) = every node on i's root path carries its parent's
-// greedy target (ancestor masks by walking parents), and the result is the
-// deepest accepted node, ties to the smallest index.
-__global__ __launch_bounds__(64) void accept_walk_kernel(
-    int N, int vsplits, const ArgBest* __restrict__ part, const int32_t* __restrict__ tokens,
-    const int32_t* __restrict__ parents, int64_t par_sb, int max_depth, int32_t* accept_len,
-    int32_t* accept_path, int32_t* bonus, uint32_t* err) {
-  const int b = blockIdx.x, lane = threadIdx.x;
+// Acceptance of sequence b from the per-slice winners: greedy target of every
+// row, accepted(i) = every node on i's root path carries its parent's target
+// (ancestor masks by walking parents), result = deepest accepted node, ties
+// to the smallest index.  Runs in one block; nodes live in the first wave.
+__device__ void accept_walk(int b, int N, int vsplits, __amdgpu_buffer_rsrc_t prs,
+                            const int32_t* __restrict__ tokens, const int32_t* __restrict__ parents,
+                            int64_t par_sb, int max_depth, int32_t* accept_len,
+                            int32_t* accept_path, int32_t* bonus, uint32_t* err) {
+  const int tid = threadIdx.x;
   __shared__ int am[kMaxNodes + 1];
   __shared__ int par_s[kMaxNodes];
-  for (int r = lane; r <= N; r += 64) {
-    const ArgBest* p = part + ((int64_t)b * (N + 1) + r) * vsplits;
-    float bv = p[0].v;
-    int bi = p[0].i;
-    for (int s = 1; s < vsplits; ++s) arg_consider(bv, bi, p[s].v, p[s].i);
-    am[r] = bi;
+  __shared__ int on_path[kMaxNodes];
+  if (tid <= N) {
+    const uint32_t p0 = (uint32_t)(((int64_t)b * (N + 1) + tid) * vsplits * sizeof(ArgBest));
+    float bv = load_sc1_f1(prs, p0);
+    int bi = __float_as_int(load_sc1_f1(prs, p0 + 4));
+    for (int s = 1; s < vsplits; ++s)
+      arg_consider(bv, bi, load_sc1_f1(prs, p0 + s * 8), __float_as_int(load_sc1_f1(prs, p0 + s * 8 + 4)));
+    am[tid] = bi;
   }
   bool bad = false;
   int pr = -1, tok = 0;
-  if (lane < N) {
-    pr = parents[b * par_sb + lane];
-    tok = tokens[(int64_t)b * N + lane];
-    par_s[lane] = pr;
-    bad = !(pr >= -1 && pr < lane);
+  if (tid < N) {
+    pr = parents[b * par_sb + tid];
+    tok = tokens[(int64_t)b * N + tid];
+    par_s[tid] = pr;
+    bad = !(pr >= -1 && pr < tid);
   }
   const bool any_bad = __syncthreads_or(bad);
   int32_t* path = accept_path + (int64_t)b * max_depth;
   if (any_bad) {
-    if (lane == 0) {
+    if (tid == 0) {
       raise_error(err, SPEC_DEV_PARENT);
       accept_len[b] = -1;
       bonus[b] = -1;
     }
-    for (int k = lane; k < max_depth; k += 64) path[k] = -1;
+    for (int k = tid; k < max_depth; k += 256) path[k] = -1;
     return;
   }
-  const bool match = lane < N && tok == am[pr + 1];
-  const uint64_t match_mask = __ballot(match);
+  int best = -1, len = 0;
   uint64_t anc = 0;
   int depth = -1;
-  if (lane < N)
-    for (int j = lane; j >= 0; j = par_s[j]) {
-      anc |= 1ull << j;
-      ++depth;
-    }
-  const bool acc = lane < N && (anc & ~match_mask) == 0;
-  // deepest accepted node, ties to the smallest index
-  int key = acc ? (depth << 8) | (255 - lane) : -1;
+  if (tid < 64) {   // N <= 64: every node is a lane of the first wavefront
+    const bool match = tid < N && tok == am[pr + 1];
+    const uint64_t match_mask = __ballot(match);
+    if (tid < N)
+      for (int j = tid; j >= 0; j = par_s[j]) {
+        anc |= 1ull << j;
+        ++depth;
+      }
+    const bool acc = tid < N && (anc & ~match_mask) == 0;
+    int key = acc ? (depth << 8) | (255 - tid) : -1;
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) key = max(key, __shfl_xor(key, m, 64));
-  const int best = key < 0 ? -1 : 255 - (key & 255);
-  const int len = key < 0 ? 0 : (key >> 8) + 1;
-  const uint64_t best_anc = best < 0 ? 0ull : __shfl(anc, best, 64);
-  __shared__ int on_path[kMaxNodes];
-  if (lane < N && ((best_anc >> lane) & 1ull)) on_path[depth] = lane;
+    for (int m = 32; m >= 1; m >>= 1) key = max(key, __shfl_xor(key, m, 64));
+    best = key < 0 ? -1 : 255 - (key & 255);
+    len = key < 0 ? 0 : (key >> 8) + 1;
+    const uint64_t best_anc = best < 0 ? 0ull : __shfl(anc, best, 64);
+    if (tid < N && ((best_anc >> tid) & 1ull)) on_path[depth] = tid;
+  }
   __syncthreads();
-  for (int k = lane; k < max_depth; k += 64) path[k] = k < len ? on_path[k] : -1;
-  if (lane == 0) {
-    if (len > max_depth) raise_error(err, SPEC_DEV_DEPTH);
-    accept_len[b] = len;
-    bonus[b] = am[best + 1];
+  if (tid < 64) {
+    for (int k = tid; k < max_depth; k += 64) path[k] = k < len ? on_path[k] : -1;
+    if (tid == 0) {
+      if (len > max_depth) raise_error(err, SPEC_DEV_DEPTH);
+      accept_len[b] = len;
+      bonus[b] = am[best + 1];
+    }
   }
 }
+
+__global__ __launch_bounds__(256) void accept_kernel(
+    const float* __restrict__ logits, int64_t V, int N, int vsplits, int64_t vchunk,
+    ArgBest* __restrict__ part, uint32_t* counters, const int32_t* __restrict__ tokens,
+    const int32_t* __restrict__ parents, int64_t par_sb, int max_depth, int32_t* accept_len,
+    int32_t* accept_path, int32_t* bonus, uint32_t* err) {
+  const int row = blockIdx.x / vsplits, sp = blockIdx.x % vsplits;
+  const int b = row / (N + 1);
+  const int64_t v0 = (int64_t)sp * vchunk;
+  const int64_t v1 = min(V, v0 + vchunk);
+  const ArgBest best = slice_argmax(logits + (int64_t)row * V, v0, v1);
+  const __amdgpu_buffer_rsrc_t prs = coherent_rsrc(part, (uint32_t)(gridDim.x * sizeof(ArgBest)));
+  if (threadIdx.x == 0) {
+    store_sc1_f1(prs, (uint32_t)(blockIdx.x * sizeof(ArgBest)), best.v);
+    store_sc1_f1(prs, (uint32_t)(blockIdx.x * sizeof(ArgBest) + 4), __int_as_float(best.i));
+  }
+  if (!arrive_last(counters + b, (N + 1) * vsplits)) return;
+  accept_walk(b, N, vsplits, prs, tokens, parents, par_sb, max_depth, accept_len, accept_path,
+              bonus, err);
+}
+
+size_t accept_part_offset(int B) { return kHeaderBytes + align_up((size_t)B * 4, 256); }
 
 hipError_t launch_accept(int B, int N, int V, const float* logits, const int32_t* tokens,
                          const int32_t* parents, int64_t parents_sb, int max_depth,
                          int32_t* accept_len, int32_t* accept_path, int32_t* bonus, void* ws,
                          int vsplits, hipStream_t st, uint32_t* err) {
-  ArgBest* part = reinterpret_cast<ArgBest*>(reinterpret_cast<uint8_t*>(ws) + kHeaderBytes);
+  uint8_t* w = reinterpret_cast<uint8_t*>(ws);
+  uint32_t* counters = reinterpret_cast<uint32_t*>(w + kHeaderBytes);
+  ArgBest* part = reinterpret_cast<ArgBest*>(w + accept_part_offset(B));
   const int64_t vchunk = cdiv(V, vsplits);
   const int64_t rows = (int64_t)B * (N + 1);
-  hipLaunchKernelGGL(argmax_partial_kernel, dim3((unsigned)(rows * vsplits)), dim3(256), 0, st,
-                     logits, (int64_t)V, vsplits, vchunk, part);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(accept_walk_kernel, dim3(B), dim3(64), 0, st, N, vsplits, part, tokens,
-                     parents, parents_sb, max_depth, accept_len, accept_path, bonus, err);
+  hipLaunchKernelGGL(accept_kernel, dim3((unsigned)(rows * vsplits)), dim3(256), 0, st, logits,
+                     (int64_t)V, N, vsplits, vchunk, part, counters, tokens, parents, parents_sb,
+                     max_depth, accept_len, accept_path, bonus, err);
   return hipGetLastError();
 }
 

@@ -6,18 +6,10 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <string>
 
 #include "spec_internal.h"
-
-namespace spec {
-hipError_t launch_draft_bf16(const AttnArgs& a, hipStream_t st);
-hipError_t launch_verify_bf16(const AttnArgs& a, hipStream_t st);
-hipError_t launch_verify_prep(const AttnArgs& a, const int32_t* parents, int64_t parents_sb,
-                              int32_t* pos_ids, uint64_t* anc_ws, int32_t* bad_ws,
-                              hipStream_t st);
-hipError_t launch_attn_f32(const AttnArgs& a, int mode, hipStream_t st);
-}  // namespace spec
 
 using namespace spec;
 
@@ -44,6 +36,7 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 int64_t esize(int dtype) { return dtype == SPEC_BF16 ? 2 : 4; }
 
 constexpr int64_t kTargetWaves = 2048;     // 256 CUs x 8 wavefronts
+constexpr int64_t kTargetWorkgroups = 512;  // 256 CUs x 2 workgroups of 4 wavefronts
 constexpr int64_t kMaxGrid = 0x7fffffff;
 
 spec_status check_dims(const spec_dims* d) {
@@ -74,55 +67,121 @@ spec_status check_kv(const spec_kv* kv, const spec_dims* d, const char* name, bo
   if (kv->stride_b % m || kv->stride_h % m || kv->stride_t % m)
     return fail(SPEC_E_INVALID, "%s strides must be multiples of %lld elements", name, (long long)m);
   if (need_cap && kv->capacity < 0) return fail(SPEC_E_INVALID, "%s.capacity %d < 0", name, kv->capacity);
-  // kernels address a 32-token tile with 32-bit byte offsets
+  // kernels address a (sequence, head)'s rows with 32-bit byte offsets
   if (kv->stride_t * (int64_t)esize(d->dtype) * 64 > INT32_MAX)
     return fail(SPEC_E_UNSUPPORTED, "%s.stride_t %lld is too large", name, (long long)kv->stride_t);
+  if (need_cap && ((int64_t)std::max(kv->capacity, 1) - 1) * kv->stride_t * esize(d->dtype) +
+                      (int64_t)d->head_dim * esize(d->dtype) > (int64_t)UINT32_MAX)
+    return fail(SPEC_E_UNSUPPORTED, "%s: capacity x stride_t spans more than 4 GiB per head", name);
   return SPEC_OK;
 }
 
 // ------------------------------------------------------------ planning
 
-Plan draft_plan(const spec_dims* d, int32_t Tq, int64_t max_view) {
+// Shape and split plan of the bf16 attention kernel (and workspace layout).
+// `tiles` is the largest number of 32-key tiles a (sequence, KV head) can
+// have; `gather` / `verify` bound the per-workgroup key range by what the
+// kernel stages in LDS (budget indices, pad bits).
+Plan bf16_plan(const spec_dims* d, int32_t T, int64_t tiles, bool gather, bool verify) {
   Plan p;
   const int G = d->n_q_heads / d->n_kv_heads;
-  p.rows = Tq * G;
   const int64_t pairs = (int64_t)d->batch * d->n_kv_heads;
-  if (d->dtype == SPEC_BF16) {
-    p.rb = p.rows <= 4 ? 4 : p.rows <= 8 ? 8 : p.rows <= 12 ? 12 : 16;
-    p.n_rb = (int32_t)cdiv(p.rows, p.rb);
-    plan_splits(p, pairs, max_view, 64, 32, kTargetWaves);
-  } else {
-    p.rb = 1;
-    p.n_rb = p.rows;
-    plan_splits(p, pairs, max_view, 64, 64, kTargetWaves);
+  p.rows = T * G;
+  int64_t ring;
+  if (p.rows <= 32) {           // few rows: four private rings per workgroup
+    p.wk = 4;
+    p.rt = (int32_t)cdiv(p.rows, 16);
+    p.rb = 16 * p.rt;
+    ring = std::max<int64_t>(4 * 128 * d->head_dim, 4 * p.rb * (d->head_dim + 2) * 4);
+  } else {                      // many rows: one shared ring, 4 x 16*rt rows
+    p.wk = 1;
+    p.rt = (int32_t)std::min<int64_t>(2, cdiv(p.rows, 64));
+    p.rb = 64 * p.rt;
+    ring = (p.rt >= 3 ? 6 : 4) * 128 * d->head_dim;
   }
-  plan_partials(p, pairs, d->head_dim);
+  p.n_rb = (int32_t)cdiv(p.rows, p.rb);
+  if (tiles < 1) tiles = 1;
+  const int64_t groups = std::max<int64_t>(1, pairs * p.n_rb);
+  int64_t S = p.wk == 4 ? std::min(cdiv(kTargetWaves, groups * 4), cdiv(tiles, 4))
+                        : std::min(cdiv(kTargetWorkgroups, groups), tiles);
+  int64_t lo = 1;
+  if (gather) lo = std::max(lo, cdiv(tiles, kMaxGatherKeys / kTileKeys));
+  if (verify) lo = std::max(lo, cdiv(tiles, kMaxPadWords));
+  S = std::min<int64_t>(std::max(S, lo), kMaxSplits);
+  if (S < lo) {
+    p.total = 0;
+    return p;
+  }
+  p.tps = (int32_t)cdiv(tiles, S);
+  p.splits = (int32_t)cdiv(tiles, p.tps);
+  p.n_blk = (int32_t)cdiv(p.splits, kMergeFan);
+  size_t off = kHeaderBytes;
+  p.cnt_off = off;
+  off = align_up(off + (size_t)(groups * (p.n_blk + 1) + 2 * std::max(0, d->batch)) * sizeof(uint32_t), 256);
+  if (p.splits > 1) {
+    const size_t n = (size_t)groups * p.splits * p.rb;
+    p.o_off = off;
+    off = align_up(off + n * d->head_dim * sizeof(float), 256);
+    p.lse_off = off;
+    off = align_up(off + n * sizeof(float), 256);
+  }
+  if (p.n_blk > 1) {
+    const size_t n = (size_t)groups * p.n_blk * p.rb;
+    p.o1_off = off;
+    off = align_up(off + n * d->head_dim * sizeof(float), 256);
+    p.lse1_off = off;
+    off = align_up(off + n * sizeof(float), 256);
+  }
+  p.total = off;
   return p;
 }
 
-Plan verify_plan(const spec_dims* d, int32_t N, int32_t capacity) {
+// fp32 path: one wavefront per (pair, row, split) and a separate combine.
+void f32_splits(Plan& p, int64_t pairs, int64_t keys) {
+  if (keys < 1) keys = 1;
+  const int64_t units = pairs * p.n_rb;
+  int64_t s = cdiv(kTargetWaves, units > 0 ? units : 1);
+  s = std::min(s, cdiv(keys, 64));
+  if (s < 1) s = 1;
+  p.chunk = (int32_t)(cdiv(cdiv(keys, s), 64) * 64);
+  p.splits = (int32_t)cdiv(keys, p.chunk);
+}
+
+Plan f32_plan(const spec_dims* d, int32_t T, int64_t keys, bool verify) {
   Plan p;
   const int G = d->n_q_heads / d->n_kv_heads;
-  p.rows = N * G;
   const int64_t pairs = (int64_t)d->batch * d->n_kv_heads;
-  const int64_t keys = capacity > 0 ? capacity : 1;
-  if (d->dtype == SPEC_BF16) {
-    p.rb = p.rows <= 16 ? 16 : 32;
-    p.n_rb = (int32_t)cdiv(p.rows, p.rb);
-    plan_splits(p, pairs, keys, 256, 32, kTargetWaves);
-  } else {
-    p.rb = 1;
-    p.n_rb = p.rows;
-    plan_splits(p, pairs, keys, 64, 64, kTargetWaves);
+  p.rows = T * G;
+  p.rb = 1;
+  p.n_rb = p.rows;
+  f32_splits(p, pairs, keys);
+  size_t off = kHeaderBytes;
+  if (p.splits > 1) {
+    const size_t n = (size_t)pairs * p.n_rb * p.splits;
+    p.o_off = off;
+    off = align_up(off + n * d->head_dim * sizeof(float), 256);
+    p.lse_off = off;
+    off = align_up(off + n * sizeof(float), 256);
   }
-  plan_partials(p, pairs, d->head_dim);
-  size_t off = p.total;
-  p.anc_off = off;
-  off = align_up(off + (size_t)d->batch * N * sizeof(uint64_t), 256);
-  p.bad_off = off;
-  off = align_up(off + (size_t)d->batch * sizeof(int32_t), 256);
+  if (verify) {
+    p.anc_off = off;
+    off = align_up(off + (size_t)d->batch * T * sizeof(uint64_t), 256);
+    p.bad_off = off;
+    off = align_up(off + (size_t)d->batch * sizeof(int32_t), 256);
+  }
   p.total = off;
   return p;
+}
+
+Plan draft_plan(const spec_dims* d, int32_t Tq, int64_t max_view, bool gather) {
+  if (d->dtype == SPEC_BF16) return bf16_plan(d, Tq, cdiv(std::max<int64_t>(max_view, 1), kTileKeys), gather, false);
+  return f32_plan(d, Tq, max_view, false);
+}
+
+Plan verify_plan(const spec_dims* d, int32_t N, int32_t capacity) {
+  if (d->dtype == SPEC_BF16)
+    return bf16_plan(d, N, cdiv(std::max(capacity, 0), kTileKeys) + cdiv(N, kTileKeys), false, true);
+  return f32_plan(d, N, std::max(capacity, 1), true);
 }
 
 int accept_vsplits(int64_t rows, int64_t V) {
@@ -134,8 +193,9 @@ int accept_vsplits(int64_t rows, int64_t V) {
   return (int)vs;
 }
 
-size_t accept_bytes(int64_t rows, int vs) {
-  return align_up(kHeaderBytes + (size_t)rows * vs * 8, 256);
+// header | per-sequence arrival counters | (value, index) winner per slice
+size_t accept_bytes(int64_t batch, int64_t rows, int vs) {
+  return align_up(kHeaderBytes + align_up((size_t)batch * 4, 256) + (size_t)rows * vs * 8, 256);
 }
 
 int64_t draft_max_view(const spec_kv* cache, int32_t Tq, int32_t n_sink, int32_t window,
@@ -143,6 +203,33 @@ int64_t draft_max_view(const spec_kv* cache, int32_t Tq, int32_t n_sink, int32_t
   if (idx != nullptr) return budget;
   int64_t v = (int64_t)n_sink + window + Tq - 1;
   return v < cache->capacity ? v : cache->capacity;
+}
+
+// Workgroups (bf16) or wavefronts (fp32) of one attention launch.
+int64_t grid_size(const spec_dims* d, const Plan& p) {
+  const int64_t units = (int64_t)d->batch * d->n_kv_heads * p.splits;
+  if (d->dtype != SPEC_BF16) return units * p.n_rb;
+  return p.n_rb == 1 ? units : cdiv(units, 8) * 8 * p.n_rb;
+}
+
+void fill_plan(AttnArgs& a, const Plan& p, void* workspace) {
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  a.rb = p.rb;
+  a.n_rb = p.n_rb;
+  a.splits = p.splits;
+  a.chunk = p.chunk;
+  a.tps = p.tps;
+  a.units = a.B * a.Hkv * p.splits;
+  a.o_part = reinterpret_cast<float*>(ws + p.o_off);
+  a.lse_part = reinterpret_cast<float*>(ws + p.lse_off);
+  a.o_part1 = reinterpret_cast<float*>(ws + p.o1_off);
+  a.lse_part1 = reinterpret_cast<float*>(ws + p.lse1_off);
+  a.n_blk = p.n_blk;
+  const size_t groups = (size_t)a.B * a.Hkv * p.n_rb;
+  a.cnt_l0 = reinterpret_cast<uint32_t*>(ws + p.cnt_off);
+  a.cnt_l1 = a.cnt_l0 + groups * p.n_blk;
+  a.cnt_pos = a.cnt_l1 + groups;
+  a.err = reinterpret_cast<uint32_t*>(ws);
 }
 
 }  // namespace
@@ -172,7 +259,10 @@ size_t spec_draft_workspace_bytes(const spec_dims* dims, int32_t n_q_tokens, int
     fail(SPEC_E_INVALID, "n_q_tokens must be >= 1 and max_view_len >= 0");
     return 0;
   }
-  return draft_plan(dims, n_q_tokens, max_view_len).total;
+  const size_t n = std::max(draft_plan(dims, n_q_tokens, max_view_len, false).total,
+                            draft_plan(dims, n_q_tokens, max_view_len, true).total);
+  if (n == 0) fail(SPEC_E_UNSUPPORTED, "no split plan fits this shape");
+  return n;
 }
 
 size_t spec_verify_workspace_bytes(const spec_dims* dims, int32_t n_nodes, int32_t capacity) {
@@ -181,7 +271,9 @@ size_t spec_verify_workspace_bytes(const spec_dims* dims, int32_t n_nodes, int32
     fail(SPEC_E_INVALID, "n_nodes must be in [1, 64] and capacity >= 0");
     return 0;
   }
-  return verify_plan(dims, n_nodes, capacity).total;
+  const size_t n = verify_plan(dims, n_nodes, capacity).total;
+  if (n == 0) fail(SPEC_E_UNSUPPORTED, "no split plan fits this shape");
+  return n;
 }
 
 size_t spec_accept_workspace_bytes(int32_t batch, int32_t n_nodes, int32_t vocab) {
@@ -190,7 +282,7 @@ size_t spec_accept_workspace_bytes(int32_t batch, int32_t n_nodes, int32_t vocab
     return 0;
   }
   const int64_t rows = (int64_t)batch * (n_nodes + 1);
-  return accept_bytes(rows, accept_vsplits(rows, vocab));
+  return accept_bytes(batch, rows, accept_vsplits(rows, vocab));
 }
 
 spec_status spec_attn_draft_sparse(const spec_dims* dims, const void* q, int32_t n_q_tokens,
@@ -219,13 +311,13 @@ spec_status spec_attn_draft_sparse(const spec_dims* dims, const void* q, int32_t
     mode = kDraftGather;
   }
   const int64_t max_view = draft_max_view(cache, n_q_tokens, n_sink, window, idx, budget);
-  const Plan p = draft_plan(dims, n_q_tokens, max_view);
+  const Plan p = draft_plan(dims, n_q_tokens, max_view, mode == kDraftGather);
+  if (p.total == 0) return fail(SPEC_E_UNSUPPORTED, "no split plan fits this shape");
   if (workspace == nullptr || workspace_bytes < p.total)
     return fail(SPEC_E_WORKSPACE, "workspace of %zu bytes needed (got %zu)", p.total,
                 workspace == nullptr ? (size_t)0 : workspace_bytes);
   if (!aligned(workspace, 256)) return fail(SPEC_E_INVALID, "workspace must be 256-byte aligned");
-  const int64_t waves = (int64_t)dims->batch * dims->n_kv_heads * p.n_rb * p.splits;
-  if (waves > kMaxGrid) return fail(SPEC_E_UNSUPPORTED, "problem too large for one launch");
+  if (grid_size(dims, p) > kMaxGrid) return fail(SPEC_E_UNSUPPORTED, "problem too large for one launch");
   if (dims->batch == 0) return SPEC_OK;
 
   AttnArgs a{};
@@ -251,22 +343,19 @@ spec_status spec_attn_draft_sparse(const spec_dims* dims, const void* q, int32_t
   a.budget = budget;
   a.idx_sb = idx_stride_b;
   a.idx_sh = idx_stride_h;
-  a.rb = p.rb;
-  a.n_rb = p.n_rb;
-  a.splits = p.splits;
-  a.chunk = p.chunk;
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  a.o_part = reinterpret_cast<float*>(ws + p.o_off);
-  a.lse_part = reinterpret_cast<float*>(ws + p.lse_off);
+  fill_plan(a, p, workspace);
   a.out = out;
   a.lse = lse_or_null;
-  a.err = reinterpret_cast<uint32_t*>(ws);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = dims->dtype == SPEC_BF16 ? launch_draft_bf16(a, s) : launch_attn_f32(a, mode, s);
-  if (e != hipSuccess) return hip_fail(e, "draft launch");
-  if (p.splits > 1) {
-    e = launch_combine(a, dims->dtype, s);
-    if (e != hipSuccess) return hip_fail(e, "combine launch");
+  hipError_t e;
+  if (dims->dtype == SPEC_BF16) {
+    e = launch_attn_bf16(a, mode, p, s);
+    if (e != hipSuccess) return hip_fail(e, "draft launch");
+  } else {
+    e = launch_attn_f32(a, mode, s);
+    if (e != hipSuccess) return hip_fail(e, "draft launch");
+    if (p.splits > 1 && (e = launch_combine(a, dims->dtype, s)) != hipSuccess)
+      return hip_fail(e, "combine launch");
   }
   return SPEC_OK;
 }
@@ -298,12 +387,12 @@ spec_status spec_attn_verify_tree(const spec_dims* dims, const void* q, int32_t 
       return fail(SPEC_E_INVALID, "pad must be 4-byte aligned with pad_stride_b %% 4 == 0 and >= capacity");
   }
   const Plan p = verify_plan(dims, n_nodes, cache->capacity);
+  if (p.total == 0) return fail(SPEC_E_UNSUPPORTED, "no split plan fits this shape");
   if (workspace == nullptr || workspace_bytes < p.total)
     return fail(SPEC_E_WORKSPACE, "workspace of %zu bytes needed (got %zu)", p.total,
                 workspace == nullptr ? (size_t)0 : workspace_bytes);
   if (!aligned(workspace, 256)) return fail(SPEC_E_INVALID, "workspace must be 256-byte aligned");
-  const int64_t waves = (int64_t)dims->batch * dims->n_kv_heads * p.n_rb * p.splits;
-  if (waves > kMaxGrid) return fail(SPEC_E_UNSUPPORTED, "problem too large for one launch");
+  if (grid_size(dims, p) > kMaxGrid) return fail(SPEC_E_UNSUPPORTED, "problem too large for one launch");
   if (dims->batch == 0) return SPEC_OK;
 
   AttnArgs a{};
@@ -330,28 +419,28 @@ spec_status spec_attn_verify_tree(const spec_dims* dims, const void* q, int32_t 
   a.tkb = tree->stride_b;
   a.tkh = tree->stride_h;
   a.tkt = tree->stride_t;
-  a.rb = p.rb;
-  a.n_rb = p.n_rb;
-  a.splits = p.splits;
-  a.chunk = p.chunk;
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  a.o_part = reinterpret_cast<float*>(ws + p.o_off);
-  a.lse_part = reinterpret_cast<float*>(ws + p.lse_off);
-  uint64_t* anc_ws = reinterpret_cast<uint64_t*>(ws + p.anc_off);
-  int32_t* bad_ws = reinterpret_cast<int32_t*>(ws + p.bad_off);
-  a.anc = anc_ws;
-  a.bad = bad_ws;
+  a.parents = parents;
+  a.par_sb = parents_stride_b;
+  a.pos_ids = pos_ids_or_null;
+  fill_plan(a, p, workspace);
   a.out = out;
   a.lse = lse_or_null;
-  a.err = reinterpret_cast<uint32_t*>(ws);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_verify_prep(a, parents, parents_stride_b, pos_ids_or_null, anc_ws, bad_ws, s);
-  if (e != hipSuccess) return hip_fail(e, "verify prep launch");
-  e = dims->dtype == SPEC_BF16 ? launch_verify_bf16(a, s) : launch_attn_f32(a, kVerify, s);
-  if (e != hipSuccess) return hip_fail(e, "verify launch");
-  if (p.splits > 1) {
-    e = launch_combine(a, dims->dtype, s);
-    if (e != hipSuccess) return hip_fail(e, "combine launch");
+  hipError_t e;
+  if (dims->dtype == SPEC_BF16) {
+    e = launch_attn_bf16(a, kVerify, p, s);
+    if (e != hipSuccess) return hip_fail(e, "verify launch");
+  } else {
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    uint64_t* anc_ws = reinterpret_cast<uint64_t*>(ws + p.anc_off);
+    int32_t* bad_ws = reinterpret_cast<int32_t*>(ws + p.bad_off);
+    a.anc = anc_ws;
+    a.bad = bad_ws;
+    e = launch_verify_prep(a, parents, parents_stride_b, pos_ids_or_null, anc_ws, bad_ws, s);
+    if (e != hipSuccess) return hip_fail(e, "verify prep launch");
+    if ((e = launch_attn_f32(a, kVerify, s)) != hipSuccess) return hip_fail(e, "verify launch");
+    if (p.splits > 1 && (e = launch_combine(a, dims->dtype, s)) != hipSuccess)
+      return hip_fail(e, "combine launch");
   }
   return SPEC_OK;
 }
@@ -377,7 +466,7 @@ spec_status spec_accept_greedy(int32_t batch, int32_t n_nodes, int32_t vocab, co
     return fail(SPEC_E_INVALID, "parents_stride_b must be 0 (shared) or >= n_nodes");
   const int64_t rows = (int64_t)batch * (n_nodes + 1);
   const int vs = accept_vsplits(rows, vocab);
-  const size_t need = accept_bytes(rows, vs);
+  const size_t need = accept_bytes(batch, rows, vs);
   if (workspace == nullptr || workspace_bytes < need)
     return fail(SPEC_E_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
                 workspace == nullptr ? (size_t)0 : workspace_bytes);

@@ -1,0 +1,876 @@
+// Draft and verify attention, bf16 inputs, fp32 accumulation (gfx950).
+//
+// Method.
+//  * Draft: "Windowed-MTP: Removing the Full-Context Draft-KV Tax at
+//    Million-Token Context" (Pith review), "What carries the argument": the
+//    draft reads only the first n_sink cached tokens plus the last W tokens;
+//    "BudgetDraft: Acceptance-Aware Multi-View Training for Sparse-KV
+//    Speculative Decoding" (Pith review), abstract: the drafter reads a sparse
+//    KV view under a fixed budget of positions.
+//  * Verify: "SpecMemo: Speculative Decoding is in Your Pocket" (Pith review),
+//    "What carries the argument" and Figure 9: the N speculated tree nodes are
+//    checked in one pass under a tree attention mask; batched verification
+//    pads accepted tokens, remaps position IDs so padding is ignored and gives
+//    cached padding slots -inf.
+//
+// One kernel serves the three key sources.  A workgroup (4 wavefronts) owns
+// one (sequence, KV head, row block, split).  Its keys arrive in 32-key tiles
+// (K and V rows, D bf16 each) copied straight from HBM into an LDS ring with
+// global_load_lds (no register staging); the copies for the next NS-1 tiles
+// are in flight while a tile is multiplied.  Both products run on bf16 MFMA
+// (v_mfma_f32_16x16x32_bf16) in transposed form:
+//     S^T[key][row] = K[key][:] . Q[row][:]
+//     O^T[d][row]  += V^T[d][key] . P^T[key][row]
+// so a lane owns one query row in both accumulators: the online softmax
+// (max, rescale, sum) stays in the lane and P goes from the score registers
+// straight into the next MFMA operand.  The V^T operand comes from V's
+// natural layout through the LDS transpose read (ds_read_b64_tr_b16).
+//
+// Two shapes:
+//  * many rows (trees: nodes x GQA group > 32): the 4 wavefronts share one
+//    ring and each owns up to 64 rows (WK = 1);
+//  * few rows (chains, drafts): each wavefront streams its own quarter of the
+//    workgroup's tiles through a private ring and the four results are merged
+//    in LDS at the end (WK = 4).
+// Several splits per (sequence, KV head) are merged by the workgroup that
+// finishes last, so a call is one launch.
+#include "dev_common.h"
+
+namespace spec {
+
+template <int D>
+struct Geo {
+  static constexpr int ROWB = 2 * D;             // bytes per key row
+  static constexpr int CH = ROWB / 16;           // 16-byte chunks per row
+  static constexpr int KB = kTileKeys * ROWB;    // K bytes per tile
+  static constexpr int SB = 2 * KB;              // stage: K then V
+  static constexpr int DPT = SB / 1024;          // 1 KB copy instructions per tile
+  static constexpr int RPI = 1024 / ROWB;        // key rows per copy instruction
+  static constexpr int ND = D / 32;              // q.k MFMA steps
+  static constexpr int NDT = D / 16;             // 16-wide head-dim tiles of O
+};
+
+// LDS swizzles (16-byte chunk index XOR a function of the key row) that make
+// the K-operand reads (16 rows at one chunk) and the transpose reads of V
+// (16 rows x 32 bytes) free of bank conflicts.
+template <int D>
+__device__ __forceinline__ int swz_k(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int r) {
+  return D == 128 ? ((r & 7) << 1) : (((r >> 1) & 3) << 1);
+}
+
+__device__ __forceinline__ bf16x8 lds_load_b128(uint32_t addr) {
+  return *SPEC_LDS(const bf16x8, (uintptr_t)addr);
+}
+
+// Wait until the copies of all but the newest `n` tiles (0 <= n <= MAXN)
+// issued by this wavefront have landed.
+template <int DPW, int MAXN>
+__device__ __forceinline__ void wait_tiles(int n) {
+  if constexpr (MAXN <= 0) {
+    wait_vm<0>();
+  } else {
+    if (n >= MAXN) wait_vm<MAXN * DPW>();
+    else wait_tiles<DPW, MAXN - 1>(n);
+  }
+}
+
+// Where the keys of one (sequence, KV head) come from.  Rows are addressed
+// with 32-bit byte offsets from the (sequence, KV head)'s first cache row or
+// first tree row; the host guarantees they fit.
+struct KeySrc {
+  const char* k;            // cache K / V rows of this (sequence, KV head)
+  const char* v;
+  const char* tk;           // tree K / V rows (verify)
+  const char* tv;
+  const int32_t* idx;       // budget positions staged in LDS (gather), from view v0
+  uint32_t rowb, trowb;     // row strides in bytes
+  uint32_t kbytes, tbytes;  // addressable bytes from k / tk
+  int n_view, cache_tiles, n_tree, s_len, w_start, v0;
+};
+
+// Key position of view position v (0 <= v < n_view).
+template <int MODE>
+__device__ __forceinline__ int view_pos(KeySrc ks, int v) {
+  if constexpr (MODE == kDraftWindow) return v < ks.s_len ? v : ks.w_start + (v - ks.s_len);
+  else if constexpr (MODE == kDraftGather) return ks.idx[v - ks.v0];
+  else return v;
+}
+
+__device__ __forceinline__ bool is_tree_tile(KeySrc ks, int t, int mode) {
+  return mode == kVerify && t >= ks.cache_tiles;
+}
+
+// Row of tile key r (0..31): the segment's row index, clamped to its last
+// row (keys past the end re-read it; their scores are masked).
+template <int MODE>
+__device__ __forceinline__ int tile_row(KeySrc ks, int t, int r) {
+  if (!is_tree_tile(ks, t, MODE)) return view_pos<MODE>(ks, min(t * kTileKeys + r, ks.n_view - 1));
+  return min((t - ks.cache_tiles) * kTileKeys + r, ks.n_tree - 1);
+}
+
+// First row of tile t if its 32 rows are consecutive rows of one segment,
+// else -1 (budget gathers, a window tile that straddles the sink, and a
+// segment's last, partial tile).
+template <int MODE>
+__device__ __forceinline__ int tile_first_row(KeySrc ks, int t) {
+  if (is_tree_tile(ks, t, MODE)) {
+    const int j0 = (t - ks.cache_tiles) * kTileKeys;
+    return j0 + kTileKeys <= ks.n_tree ? j0 : -1;
+  }
+  const int v = t * kTileKeys;
+  if (v + kTileKeys > ks.n_view) return -1;
+  if constexpr (MODE == kDraftWindow) {
+    if (v + kTileKeys <= ks.s_len) return v;
+    if (v >= ks.s_len) return ks.w_start + (v - ks.s_len);
+    return -1;
+  } else if constexpr (MODE == kDraftGather) {
+    return -1;
+  } else {
+    return v;
+  }
+}
+
+// Issue this wavefront's share (DPW of the tile's 1 KB copies) of tile t into
+// the LDS stage at `stage`.  Copy gi covers key rows (gi % (DPT/2)) * RPI ..
+// of K (first half) or V (second half); lane l writes 16-byte slot l % CH of
+// row l / CH, which holds head-dim chunk (slot XOR swizzle(row)).
+template <int MODE, int D, int DPW>
+__device__ __forceinline__ void issue_tile(KeySrc ks, int t, uint32_t stage, int wl, int lane) {
+  using Ge = Geo<D>;
+  const bool tree = is_tree_tile(ks, t, MODE);
+  const int j0 = tile_first_row<MODE>(ks, t);
+  const bool contig = j0 >= 0;
+  const uint32_t rowb = tree ? ks.trowb : ks.rowb;
+#pragma unroll
+  for (int u = 0; u < DPW; ++u) {
+    const int gi = wl * DPW + u;
+    const int region = gi / (Ge::DPT / 2);    // 0: K, 1: V
+    const int ii = gi % (Ge::DPT / 2);
+    const int rl = lane / Ge::CH;
+    const int r = ii * Ge::RPI + rl;
+    const uint32_t col = (uint32_t)(((lane % Ge::CH) ^ (region ? swz_v<D>(r) : swz_k<D>(r))) * 16);
+    const char* seg = tree ? (region ? ks.tv : ks.tk) : (region ? ks.v : ks.k);
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(stage + region * Ge::KB + ii * 1024);
+    if (contig) {
+      const char* sb = seg + (size_t)(j0 + ii * Ge::RPI) * rowb;   // wave-uniform
+      copy16_to_lds(sb + ((uint32_t)rl * rowb + col), m0);
+    } else {
+      const int j = tile_row<MODE>(ks, t, r);
+      copy16_to_lds(seg + ((uint32_t)j * rowb + col), m0);
+    }
+  }
+}
+
+// Register-staged tile (one wavefront loads all of it): piece gi of the tile
+// is K (first half) or V rows (gi % (DPT/2)) * RPI + lane / CH, head-dim
+// chunk lane % CH, loaded with coalesced 16-byte buffer loads (streaming
+// hint; out-of-range offsets read zeros instead of faulting) ...
+template <int MODE, int D>
+__device__ __forceinline__ void load_tile_regs(KeySrc ks, int t, int lane, u32x4 (&stg)[Geo<D>::DPT]) {
+  using Ge = Geo<D>;
+  constexpr int kNt = 2;   // cache policy: non-temporal
+  const bool tree = is_tree_tile(ks, t, MODE);
+  const int j0 = tile_first_row<MODE>(ks, t);
+  const bool contig = j0 >= 0;
+  const uint32_t rowb = tree ? ks.trowb : ks.rowb;
+  const __amdgpu_buffer_rsrc_t rk = coherent_rsrc(tree ? ks.tk : ks.k, tree ? ks.tbytes : ks.kbytes);
+  const __amdgpu_buffer_rsrc_t rv = coherent_rsrc(tree ? ks.tv : ks.v, tree ? ks.tbytes : ks.kbytes);
+  const int rl = lane / Ge::CH;
+  const uint32_t col = (uint32_t)((lane % Ge::CH) * 16);
+  constexpr int H = Ge::DPT / 2;
+  // Offsets first (lane offset fixed and row offset in the scalar soffset for
+  // a contiguous tile; per-lane rows otherwise), then one burst of loads into
+  // the staging registers: a single definition of each register lets the
+  // compiler load the next tile in place instead of into temporaries it would
+  // have to wait for and copy at the end of the iteration.
+  uint32_t voff[Ge::DPT], soff[Ge::DPT];
+  if (contig) {
+    const uint32_t s0 = (uint32_t)j0 * rowb;
+#pragma unroll
+    for (int gi = 0; gi < Ge::DPT; ++gi) {
+      voff[gi] = (uint32_t)rl * rowb + col;
+      soff[gi] = s0 + (uint32_t)((gi % H) * Ge::RPI) * rowb;
+    }
+  } else {
+#pragma unroll
+    for (int gi = 0; gi < Ge::DPT; ++gi) {
+      voff[gi] = (uint32_t)tile_row<MODE>(ks, t, (gi % H) * Ge::RPI + rl) * rowb + col;
+      soff[gi] = 0;
+    }
+  }
+#pragma unroll
+  for (int gi = 0; gi < Ge::DPT; ++gi)
+    stg[gi] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(gi < H ? rk : rv, voff[gi], soff[gi], kNt));
+}
+// ... and written to the wavefront's LDS stage at its swizzled slot.
+template <int D>
+__device__ __forceinline__ void store_tile_lds(uint32_t stage, int lane, const u32x4 (&stg)[Geo<D>::DPT]) {
+  using Ge = Geo<D>;
+#pragma unroll
+  for (int gi = 0; gi < Ge::DPT; ++gi) {
+    const int region = gi / (Ge::DPT / 2);
+    const int r = (gi % (Ge::DPT / 2)) * Ge::RPI + lane / Ge::CH;
+    const int p = (lane % Ge::CH) ^ (region ? swz_v<D>(r) : swz_k<D>(r));
+    *SPEC_LDS(u32x4, (uintptr_t)(stage + region * Ge::KB + r * Ge::ROWB + p * 16)) = stg[gi];
+  }
+}
+
+// Merge n (1..kMergeFan) partial results of RC rows: partial p of row rl is
+// o (normalised by its own softmax sum) at o_rs[((p0 + p) * RC + rl) * D + d]
+// and its log2 sum-exp at l_rs[(p0 + p) * RC + rl].  For every (row, 4 head-
+// dim values) item of the first `rows` rows, all loads are issued before any
+// is used (partials past n re-read the last one and get weight 0), and
+// sink(rl, d0, o[4], lse2) receives sum_p 2^(x_p - M) o_p / sum_p 2^(x_p - M)
+// and M + log2 sum_p 2^(x_p - M), M = max_p x_p: NaN if any partial is NaN,
+// o = 0 and lse = -inf if every partial is empty.
+template <int D, int RC, typename Sink>
+__device__ __forceinline__ void merge_partials(__amdgpu_buffer_rsrc_t o_rs, __amdgpu_buffer_rsrc_t l_rs,
+                                               int p0, int n, int rows, Sink sink) {
+  for (int it = threadIdx.x; it < RC * (D / 4); it += 256) {
+    const int rl = it / (D / 4), d0 = (it % (D / 4)) * 4;
+    if (rl >= rows) continue;
+    float x[kMergeFan];
+    f32x4 ov[kMergeFan];
+#pragma unroll
+    for (int p = 0; p < kMergeFan; ++p) {
+      const int pp = p0 + min(p, n - 1);
+      x[p] = load_sc1_f1(l_rs, (uint32_t)((pp * RC + rl) * 4));
+      ov[p] = load_sc1_f4(o_rs, (uint32_t)(((pp * RC + rl) * D + d0) * 4));
+    }
+    float M = -INFINITY;
+    bool nan = false;
+#pragma unroll
+    for (int p = 0; p < kMergeFan; ++p)
+      if (p < n) {
+        nan |= isnan(x[p]);
+        M = fmaxf(M, x[p]);
+      }
+    float W = 0.f, o[4] = {0.f, 0.f, 0.f, 0.f};
+    if (!nan && M != -INFINITY) {
+#pragma unroll
+      for (int p = 0; p < kMergeFan; ++p) {
+        const float f = p < n ? __builtin_amdgcn_exp2f(x[p] - M) : 0.f;
+        W += f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] += f * ov[p][e];
+      }
+    }
+    float lse2;
+    if (nan) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = NAN;
+      lse2 = NAN;
+    } else if (M == -INFINITY || !(W > 0.f)) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = 0.f;
+      lse2 = -INFINITY;
+    } else {
+      const float inv = 1.f / W;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] *= inv;
+      lse2 = M + log2f(W);
+    }
+    sink(rl, d0, o, lse2);
+  }
+}
+
+template <int MODE, int D, int RT, int WK, int NS>
+struct AttnCfg {
+  static constexpr int WR = 4 / WK;                 // wavefronts per key group
+  static constexpr int RCW = RT * 16;               // rows per wavefront
+  static constexpr int RC = WR * RCW;               // rows per workgroup
+  static constexpr int DPW = Geo<D>::DPT / WR;      // copies per tile per loading wave
+  // LDS: one shared ring of NS stages (WK = 1), or one stage per wavefront
+  // (WK = 4), which the end-of-split merge of the four wavefronts reuses.
+  static constexpr int MERGE = 4 * RC * (D + 2) * 4;
+  static constexpr int RING = WK == 1 ? NS * Geo<D>::SB
+                                      : (4 * Geo<D>::SB > MERGE ? 4 * Geo<D>::SB : MERGE);
+  static_assert(Geo<D>::DPT % WR == 0, "tile copies must split evenly");
+  static_assert(WK == 1 || WK == 4, "one shared ring or four private rings");
+};
+
+template <int MODE, int D, int RT, int WK, int NS>
+__global__ __launch_bounds__(256, ((WK == 4 ? RT == 1 : RT <= 2) && 2 * AttnCfg<MODE, D, RT, WK, NS>::RING <= 136 * 1024) ? 2 : 1)
+void attn_bf16_kernel(AttnArgs a) {
+  using Cf = AttnCfg<MODE, D, RT, WK, NS>;
+  using Ge = Geo<D>;
+  constexpr int WR = Cf::WR, RCW = Cf::RCW, RC = Cf::RC, DPW = Cf::DPW;
+  constexpr int ND = Ge::ND, NDT = Ge::NDT, ROWB = Ge::ROWB, CH = Ge::CH, KB = Ge::KB,
+                SB = Ge::SB, RPI = Ge::RPI;
+
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[Cf::RING];
+  __shared__ uint32_t padbits_s[MODE == kVerify ? kMaxPadWords : 1];
+  __shared__ int32_t idx_s[MODE == kDraftGather ? kMaxGatherKeys : 1];
+  __shared__ int32_t par_s[MODE == kVerify ? kMaxNodes : 1];
+  __shared__ int32_t dep_s[MODE == kVerify ? kMaxNodes : 1];
+  __shared__ uint64_t anc_s[MODE == kVerify ? kMaxNodes : 1];
+  __shared__ int32_t red_s[4];
+
+  // ---------------------------------------------------------------- who am I
+  int unit, z;
+  if (a.n_rb == 1) {
+    unit = blockIdx.x;
+    z = 0;
+  } else {
+    // The row blocks of one (pair, split) read the same keys: give them
+    // consecutive slots on one XCD (workgroups go to XCDs round-robin) so
+    // they meet in that XCD's L2.
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    unit = (slot / a.n_rb) * 8 + xcd;
+    z = slot % a.n_rb;
+    if (unit >= a.units) return;
+  }
+  const int s = unit % a.splits, pair = unit / a.splits;
+  const int b = pair / a.Hkv, g = pair % a.Hkv;
+  // (the wave index is uniform within a wavefront; saying so keeps
+  // everything derived from it, such as a wavefront's tile range and its
+  // buffer descriptors, in scalar registers)
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, q4 = lane >> 4;
+  const int kgi = WK == 1 ? 0 : wave;   // key group (ring) of this wavefront
+  const int rg = WK == 1 ? wave : 0;    // row group of this wavefront
+  const bool leader = g == 0 && s == 0 && z == 0;
+  const int T = a.T, G = a.G, N = a.T;
+
+  const int L = a.cache_len[b];
+  bool bad = MODE == kVerify ? (L < 0 || L > a.capacity) : (L < T || L > a.capacity);
+  if (leader && tid == 0 && bad) raise_error(a.err, SPEC_DEV_CACHE_LEN);
+
+  // ---------------------------------------------------------------- tree
+  if constexpr (MODE == kVerify) {
+    bool bp = false;
+    if (tid < N) {
+      const int p = a.parents[b * a.par_sb + tid];
+      par_s[tid] = p;
+      bp = !(p >= -1 && p < tid);
+    }
+    const bool bad_par = __syncthreads_or(bp);
+    if (tid < N) {
+      uint64_t m = 0;
+      int depth = -1;
+      if (!bad_par)
+        for (int j = tid; j >= 0; j = par_s[j]) {   // parents precede children: ends
+          m |= 1ull << j;
+          ++depth;
+        }
+      anc_s[tid] = m;
+      dep_s[tid] = depth;
+    }
+    if (leader && tid == 0 && bad_par) raise_error(a.err, SPEC_DEV_PARENT);
+    bad = bad || bad_par;
+  }
+
+  // ---------------------------------------------------------------- key range
+  int s_len = 0, w_start = 0, n_view = 0;
+  if (!bad) {
+    if constexpr (MODE == kDraftWindow) {
+      s_len = min(a.n_sink, L);
+      w_start = min(max(max(a.n_sink, L - T + 1 - a.window), 0), L);
+      n_view = s_len + (L - w_start);
+    } else if constexpr (MODE == kDraftGather) {
+      n_view = a.budget;
+    } else {
+      n_view = L;
+    }
+  }
+  const int cache_tiles = (n_view + kTileKeys - 1) / kTileKeys;
+  const int tree_tiles = (MODE == kVerify && !bad) ? (N + kTileKeys - 1) / kTileKeys : 0;
+  const int total = cache_tiles + tree_tiles;
+  const int t0 = min(total, s * a.tps);
+  const int t1 = min(total, t0 + a.tps);
+  int k0 = t0, k1 = t1;
+  if constexpr (WK == 4) {
+    const int per = (t1 - t0 + 3) / 4;
+    k0 = min(t1, t0 + kgi * per);
+    k1 = min(t1, k0 + per);
+  }
+
+  // ---------------------------------------------------------------- staging
+  bool poison = bad;
+  int pad_count = 0;
+  if constexpr (MODE == kDraftGather) {
+    const int v_end = min(t1 * kTileKeys, n_view);
+    const int cnt = max(0, v_end - t0 * kTileKeys);
+    const int32_t* ib = a.idx + b * a.idx_sb + g * a.idx_sh + t0 * kTileKeys;
+    bool bi = false;
+    for (int i = tid; i < cnt; i += 256) {
+      const int j = ib[i];
+      idx_s[i] = j;
+      bi |= (j < 0 || j >= L);
+    }
+    const bool bad_idx = __syncthreads_or(bi);
+    if (bad_idx && tid == 0) raise_error(a.err, SPEC_DEV_INDEX);
+    poison = poison || bad_idx;
+    if (bad_idx) k1 = k0;   // never address a position outside the cache
+  } else if constexpr (MODE == kVerify) {
+    const int wend = min(t1, cache_tiles);
+    int cnt = 0;
+    if (a.pad != nullptr) {
+      const uint8_t* prow = a.pad + b * a.pad_sb;
+      for (int w = t0 + tid; w < wend; w += 256) {
+        uint32_t bits = 0;
+        const int key0 = w * kTileKeys;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int kk = key0 + 4 * k;
+          if (kk < L) {
+            const uint32_t d = *reinterpret_cast<const uint32_t*>(prow + kk);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (kk + e < L && ((d >> (8 * e)) & 0xffu)) bits |= 1u << (4 * k + e);
+          }
+        }
+        padbits_s[w - t0] = bits;
+        cnt += __popc(bits);
+      }
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) cnt += __shfl_xor(cnt, m, 64);
+    if (lane == 0) red_s[wave] = cnt;
+    __syncthreads();
+    pad_count = red_s[0] + red_s[1] + red_s[2] + red_s[3];
+  } else {
+    __syncthreads();
+  }
+
+  // ---------------------------------------------------------------- rows
+  bf16x8 qf[RT][ND];
+  int erow[RT];
+  uint64_t ancr[RT];
+  const int row0 = z * RC + rg * RCW;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int row = row0 + rt * 16 + l16;
+    erow[rt] = 0;
+    ancr[rt] = 0;
+#pragma unroll
+    for (int c = 0; c < ND; ++c) qf[rt][c] = bf16x8{};
+    if (row < a.R) {
+      const int t = row / G, hh = row % G;
+      erow[rt] = L - T + t + 1;
+      if constexpr (MODE == kVerify) ancr[rt] = anc_s[t];
+      const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
+                           (((size_t)b * T + t) * a.Hq + g * G + hh) * D + q4 * 8;
+#pragma unroll
+      for (int c = 0; c < ND; ++c)
+        qf[rt][c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + c * 32));
+    }
+  }
+
+  // ---------------------------------------------------------------- tile copies
+  KeySrc ks;
+  ks.k = reinterpret_cast<const char*>(reinterpret_cast<const uint16_t*>(a.k) + b * a.kb + g * a.kh);
+  ks.v = reinterpret_cast<const char*>(reinterpret_cast<const uint16_t*>(a.v) + b * a.kb + g * a.kh);
+  ks.tk = ks.k;
+  ks.tv = ks.v;
+  ks.rowb = (uint32_t)(a.kt * 2);
+  ks.trowb = ks.rowb;
+  ks.kbytes = (uint32_t)min((int64_t)0xffffffff, (int64_t)max(a.capacity - 1, 0) * a.kt * 2 + 2 * D);
+  ks.tbytes = ks.kbytes;
+  if constexpr (MODE == kVerify) {
+    ks.tk = reinterpret_cast<const char*>(reinterpret_cast<const uint16_t*>(a.tk) + b * a.tkb + g * a.tkh);
+    ks.tv = reinterpret_cast<const char*>(reinterpret_cast<const uint16_t*>(a.tv) + b * a.tkb + g * a.tkh);
+    ks.trowb = (uint32_t)(a.tkt * 2);
+    ks.tbytes = (uint32_t)((int64_t)(N - 1) * a.tkt * 2 + 2 * D);
+  }
+  ks.idx = idx_s;
+  ks.n_view = n_view;
+  ks.cache_tiles = cache_tiles;
+  ks.n_tree = N;
+  ks.s_len = s_len;
+  ks.w_start = w_start;
+  ks.v0 = t0 * kTileKeys;
+  const uint32_t ring_base = lds_addr(ring) + kgi * (WK == 1 ? NS : 1) * SB;
+  const int wl = WK == 1 ? wave : 0;   // index of this wavefront among the loaders
+
+  // ---------------------------------------------------------------- main loop
+  f32x4 acc[RT][NDT];
+  float m[RT], lsum[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    m[rt] = -INFINITY;
+    lsum[rt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) acc[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const float c2 = a.scale_log2;
+  const bool row_masks = MODE != kVerify && T > 1;
+
+  // Nothing but ring copies may be in flight from here on.  The wait is the
+  // compiler's own intrinsic, so it knows the query loads are complete and
+  // inserts no memory-counter wait inside the loop (which, counting the
+  // ring copies too, would drain the prefetch pipeline every tile).
+  __builtin_amdgcn_s_waitcnt(0);
+  u32x4 stg[WK == 4 ? Ge::DPT : 1];
+  if constexpr (WK == 1) {
+#pragma unroll
+    for (int u = 0; u < NS - 1; ++u)
+      if (k0 + u < k1) issue_tile<MODE, D, DPW>(ks, k0 + u, ring_base + u * SB, wl, lane);
+  } else {
+    if (k0 < k1) load_tile_regs<MODE, D>(ks, k0, lane, stg);
+  }
+
+  for (int t = k0; t < k1; ++t) {
+    const int i = t - k0;
+    uint32_t sb;
+    if constexpr (WK == 1) {
+      wait_tiles<DPW, NS - 2>(k1 - 1 - t);
+      barrier_only();   // every wave's copies of tile t landed; tile t-1 is consumed
+      if (t + NS - 1 < k1) issue_tile<MODE, D, DPW>(ks, t + NS - 1, ring_base + ((i + NS - 1) % NS) * SB, wl, lane);
+      sb = ring_base + (i % NS) * SB;
+    } else {
+      // the wave's own stage: LDS operations of a wave execute in order, so
+      // these writes land after the previous tile's reads and before this
+      // tile's; the next tile's loads are in flight while this one is used
+      sb = ring_base;
+      store_tile_lds<D>(sb, lane, stg);
+      if (t + 1 < k1) load_tile_regs<MODE, D>(ks, t + 1, lane, stg);
+    }
+    const bool tree_tile = MODE == kVerify && t >= cache_tiles;
+
+    // K fragments (A operand of S^T): key h*16 + l16, head-dim chunk cc*4 + q4
+    bf16x8 kf[2][ND];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = h * 16 + l16;
+#pragma unroll
+      for (int cc = 0; cc < ND; ++cc)
+        kf[h][cc] = lds_load_b128(sb + r * ROWB + (((cc * 4 + q4) ^ swz_k<D>(r)) * 16));
+    }
+    f32x4 sc[RT][2];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int cc = 0; cc < ND; ++cc)
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[h][cc], qf[rt][cc], c, 0, 0, 0);
+        sc[rt][h] = c;
+      }
+
+    // Visibility of this lane's 8 keys, local index e = h*4 + i, tile key
+    // h*16 + q4*4 + i.  `full` tiles (every key visible to every row) skip it.
+    uint32_t kmask = 0xffu;
+    bool full = !tree_tile && (t + 1) * kTileKeys <= n_view && !row_masks;
+    if constexpr (MODE == kVerify) {
+      if (!tree_tile) {
+        const uint32_t pw = a.pad != nullptr ? padbits_s[t - t0] : 0u;
+        full = full && pw == 0u;
+        if (!full) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int kk = (e >> 2) * 16 + q4 * 4 + (e & 3);
+            if (t * kTileKeys + kk >= n_view || ((pw >> kk) & 1u)) kmask &= ~(1u << e);
+          }
+        }
+      }
+    } else if (!full) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int kk = (e >> 2) * 16 + q4 * 4 + (e & 3);
+        if (t * kTileKeys + kk >= n_view) kmask &= ~(1u << e);
+      }
+    }
+    int jpos[8];
+    if (row_masks) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int kk = (e >> 2) * 16 + q4 * 4 + (e & 3);
+        jpos[e] = view_pos<MODE>(ks, min(t * kTileKeys + kk, n_view - 1));
+      }
+    }
+
+    // Scores of this lane's row in the scaled log2 domain, masked.
+    float x[RT][8], mnew[RT];
+    bool grow = false;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[rt][e] = sc[rt][e >> 2][e & 3];
+      if (!full) {
+        uint32_t rm = kmask;
+        if (tree_tile) {
+          const uint32_t aw = (uint32_t)(ancr[rt] >> ((t - cache_tiles) * kTileKeys));
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int kk = (e >> 2) * 16 + q4 * 4 + (e & 3);
+            if (!((aw >> kk) & 1u)) rm &= ~(1u << e);
+          }
+        } else if (row_masks) {
+          const int er = erow[rt];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            bool vis = jpos[e] < er;
+            if (MODE == kDraftWindow) vis = vis && (jpos[e] < a.n_sink || jpos[e] >= er - a.window);
+            if (!vis) rm &= ~(1u << e);
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[rt][e] = ((rm >> e) & 1u) ? x[rt][e] : -INFINITY;
+      }
+      float mx = x[rt][0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[rt][e]);
+      mx = fmaxf(mx, shfl_xor(mx, 16));
+      mx = fmaxf(mx, shfl_xor(mx, 32));
+      mnew[rt] = mx * c2;
+      // First visible key of the row: nothing accumulated yet, just set m.
+      if (m[rt] == -INFINITY) m[rt] = mnew[rt];
+      grow = grow || mnew[rt] > m[rt] + 8.f;
+    }
+    // Lazy rescale: keep the running maximum unless a row's new maximum
+    // exceeds it by more than 2^8 (until then p <= 256, safe in fp32 and
+    // bf16); the final o = acc / l is the same either way.  The branch is
+    // wave-uniform and rare, so the accumulators stay in the MFMA registers.
+    if (__builtin_expect(__any(grow), 0)) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const bool up = mnew[rt] > m[rt] + 8.f;
+        const float alpha = up ? __builtin_amdgcn_exp2f(m[rt] - mnew[rt]) : 1.f;
+        lsum[rt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) acc[rt][dt] *= alpha;
+        m[rt] = up ? mnew[rt] : m[rt];
+      }
+    }
+    uint32_t pf[RT][4];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const float mb = m[rt] == -INFINITY ? 0.f : m[rt];
+      float p[8], ps = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = __builtin_amdgcn_exp2f(fmaf(x[rt][e], c2, -mb));
+        ps += p[e];
+      }
+      lsum[rt] += ps;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) pf[rt][w] = pack_bf16x2(p[2 * w], p[2 * w + 1]);
+    }
+
+    // O^T += V^T . P^T: V^T operand by two transpose reads per 16-wide d tile
+    // (keys 4*q4 + j, then 16 + 4*q4 + j, at d = dt*16 + l16).
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      uint32_t vaddr[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = 16 * h + 4 * q4 + (l16 >> 2);
+        const int byte = (dt * 16 + 4 * (l16 & 3)) * 2;
+        vaddr[h] = sb + KB + r * ROWB + (((byte >> 4) ^ swz_v<D>(r)) << 4) + (byte & 15);
+      }
+      const s16x4 v0 = lds_read_tr16(vaddr[0]);
+      const s16x4 v1 = lds_read_tr16(vaddr[1]);
+      const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(pf[rt][0], pf[rt][1], pf[rt][2], pf[rt][3]));
+        acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb, acc[rt][dt], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---------------------------------------------------------------- positions
+  if constexpr (MODE == kVerify) {
+    if (a.pos_ids != nullptr && g == 0 && z == 0) {
+      int n_pad = 0;
+      bool write = false;
+      if (a.pad == nullptr) {
+        write = s == 0;
+      } else {
+        // every split of head 0 counted its own range; the last one writes
+        uint32_t* cnt = a.cnt_pos + 2 * b;
+        if (tid == 0 && pad_count)
+          __hip_atomic_fetch_add(cnt + 1, (uint32_t)pad_count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        write = arrive_last(cnt, a.splits);
+        if (write && tid == 0)
+          red_s[0] = (int)__hip_atomic_exchange(cnt + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        n_pad = red_s[0];
+      }
+      if (write && tid < N) a.pos_ids[(size_t)b * N + tid] = bad ? -1 : (L - n_pad) + dep_s[tid];
+    }
+  }
+
+  // ---------------------------------------------------------------- results
+  float lr[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    lr[rt] = lsum[rt];
+    lr[rt] += shfl_xor(lr[rt], 16);
+    lr[rt] += shfl_xor(lr[rt], 32);
+  }
+  const int S = a.splits;
+  const size_t grp = (size_t)pair * a.n_rb + z;
+  // this group's partials: o [S][RC][D], lse [S][RC] (log2 domain)
+  const __amdgpu_buffer_rsrc_t o_rs = coherent_rsrc(a.o_part + grp * S * RC * D, (uint32_t)(S * RC * D * 4));
+  const __amdgpu_buffer_rsrc_t l_rs = coherent_rsrc(a.lse_part + grp * S * RC, (uint32_t)(S * RC * 4));
+  const int R = a.R, Hq = a.Hq;
+  uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
+  float* lse_out = a.lse;
+
+  // store one row's result: final output (S == 1) or this split's partial
+  auto store_row = [&](int row_l, int d0, const float* vals, bool lse_lane, float lse2)
+                       __attribute__((always_inline)) {
+    const int row = z * RC + row_l;
+    if (row >= R) return;
+    if (S > 1) {
+      store_sc1_f4(o_rs, (uint32_t)(((s * RC + row_l) * D + d0) * 4), f32x4{vals[0], vals[1], vals[2], vals[3]});
+      if (lse_lane) store_sc1_f1(l_rs, (uint32_t)((s * RC + row_l) * 4), lse2);
+      return;
+    }
+    const int t = row / G, hh = row % G;
+    const size_t oi = ((size_t)b * T + t) * Hq + g * G + hh;
+    *reinterpret_cast<uint2*>(out + oi * D + d0) =
+        make_uint2(pack_bf16x2(vals[0], vals[1]), pack_bf16x2(vals[2], vals[3]));
+    if (lse_lane && lse_out != nullptr) lse_out[oi] = lse2 * kLn2;
+  };
+
+  if constexpr (WK == 1) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      float inv, lse2;
+      if (poison) {
+        inv = NAN;
+        lse2 = NAN;
+      } else if (lr[rt] > 0.f) {
+        inv = 1.f / lr[rt];
+        lse2 = m[rt] + log2f(lr[rt]);
+      } else {
+        inv = 0.f;
+        lse2 = -INFINITY;
+      }
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        float vals[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vals[e] = poison ? NAN : acc[rt][dt][e] * inv;
+        store_row(rg * RCW + rt * 16 + l16, dt * 16 + q4 * 4, vals, q4 == 0 && dt == 0, lse2);
+      }
+    }
+  } else {
+    // merge the four wavefronts' running states through LDS
+    __syncthreads();
+    float* ms = reinterpret_cast<float*>(ring);   // [4][RC]
+    float* ls = ms + 4 * RC;                      // [4][RC]
+    float* os = ls + 4 * RC;                      // [4][RC][D]
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int rl = rt * 16 + l16;
+      if (q4 == 0) {
+        ms[wave * RC + rl] = m[rt];
+        ls[wave * RC + rl] = lr[rt];
+      }
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+        *reinterpret_cast<f32x4*>(os + ((size_t)wave * RC + rl) * D + dt * 16 + q4 * 4) = acc[rt][dt];
+    }
+    __syncthreads();
+    for (int it = tid; it < RC * (D / 4); it += 256) {
+      const int rl = it / (D / 4), d0 = (it % (D / 4)) * 4;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) M = fmaxf(M, ms[w * RC + rl]);
+      float W = 0.f, o[4] = {0.f, 0.f, 0.f, 0.f};
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float f = __builtin_amdgcn_exp2f(ms[w * RC + rl] - M);
+          W += f * ls[w * RC + rl];
+          const f32x4 ov = *reinterpret_cast<const f32x4*>(os + ((size_t)w * RC + rl) * D + d0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] += f * ov[e];
+        }
+      }
+      float lse2;
+      if (poison) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = NAN;
+        lse2 = NAN;
+      } else if (W > 0.f) {
+        const float inv = 1.f / W;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] *= inv;
+        lse2 = M + log2f(W);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = 0.f;
+        lse2 = -INFINITY;
+      }
+      store_row(rl, d0, o, d0 == 0, lse2);
+    }
+  }
+  if (S == 1) return;
+
+  // ---------------------------------------------------------------- split merge
+  // Two levels: the last of each block of up to kMergeFan splits merges the
+  // block; with more than one block, the last block merger merges the block
+  // results.  Every merge reads at most kMergeFan partials.
+  const int rows = min(RC, a.R - z * RC);
+  const int nb = a.n_blk;
+  const int blk = s / kMergeFan, bsz = min(kMergeFan, S - blk * kMergeFan);
+  auto final_sink = [&](int rl, int d0, const float* o, float lse2) __attribute__((always_inline)) {
+    const int row = z * RC + rl;
+    const int t = row / G, hh = row % G;
+    const size_t oi = ((size_t)b * T + t) * Hq + g * G + hh;
+    *reinterpret_cast<uint2*>(out + oi * D + d0) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+    if (d0 == 0 && lse_out != nullptr) lse_out[oi] = lse2 * kLn2;
+  };
+  if (!arrive_last(a.cnt_l0 + grp * nb + blk, bsz)) return;
+  if (nb == 1) {
+    merge_partials<D, RC>(o_rs, l_rs, 0, S, rows, final_sink);
+    return;
+  }
+  const __amdgpu_buffer_rsrc_t o1_rs = coherent_rsrc(a.o_part1 + grp * nb * RC * D, (uint32_t)(nb * RC * D * 4));
+  const __amdgpu_buffer_rsrc_t l1_rs = coherent_rsrc(a.lse_part1 + grp * nb * RC, (uint32_t)(nb * RC * 4));
+  merge_partials<D, RC>(o_rs, l_rs, blk * kMergeFan, bsz, rows,
+                        [&](int rl, int d0, const float* o, float lse2) __attribute__((always_inline)) {
+                          store_sc1_f4(o1_rs, (uint32_t)(((blk * RC + rl) * D + d0) * 4), f32x4{o[0], o[1], o[2], o[3]});
+                          if (d0 == 0) store_sc1_f1(l1_rs, (uint32_t)((blk * RC + rl) * 4), lse2);
+                        });
+  if (!arrive_last(a.cnt_l1 + grp, nb)) return;
+  merge_partials<D, RC>(o1_rs, l1_rs, 0, nb, rows, final_sink);
+}
+
+// ------------------------------------------------------------------ launch
+
+template <int MODE, int D, int RT, int WK>
+static hipError_t launch_shape(const AttnArgs& a, hipStream_t st) {
+  constexpr int NS = WK == 1 ? (RT >= 3 ? 6 : 4) : 1;
+  int64_t grid = a.units;
+  if (a.n_rb > 1) grid = cdiv(a.units, 8) * 8 * a.n_rb;
+  hipLaunchKernelGGL((attn_bf16_kernel<MODE, D, RT, WK, NS>), dim3((unsigned)grid), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int MODE, int D>
+static hipError_t launch_mode(const AttnArgs& a, const Plan& p, hipStream_t st) {
+  if (p.wk == 4) {
+    if (p.rt == 1) return launch_shape<MODE, D, 1, 4>(a, st);
+    return launch_shape<MODE, D, 2, 4>(a, st);
+  }
+  switch (p.rt) {
+    case 1: return launch_shape<MODE, D, 1, 1>(a, st);
+    case 2: return launch_shape<MODE, D, 2, 1>(a, st);
+    case 3: return launch_shape<MODE, D, 3, 1>(a, st);
+    default: return launch_shape<MODE, D, 4, 1>(a, st);
+  }
+}
+
+hipError_t launch_attn_bf16(const AttnArgs& a, int mode, const Plan& p, hipStream_t st) {
+  if (a.D == 128) {
+    if (mode == kDraftWindow) return launch_mode<kDraftWindow, 128>(a, p, st);
+    if (mode == kDraftGather) return launch_mode<kDraftGather, 128>(a, p, st);
+    return launch_mode<kVerify, 128>(a, p, st);
+  }
+  if (mode == kDraftWindow) return launch_mode<kDraftWindow, 64>(a, p, st);
+  if (mode == kDraftGather) return launch_mode<kDraftGather, 64>(a, p, st);
+  return launch_mode<kVerify, 64>(a, p, st);
+}
+
+}  // namespace spec

@@ -1,5 +1,6 @@
 // Device helpers shared by the gfx950 kernels: bf16 conversion, cross-lane
-// reductions, partial-result stores.
+// reductions, LDS transpose reads, direct global-to-LDS copies and explicit
+// memory-counter waits.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -12,19 +13,15 @@ namespace spec {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+#define SPEC_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
 
 // 16-byte streaming load (non-temporal hint: the data is read once).
-__device__ __forceinline__ uint4 load_stream(const void* p) {
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
 __device__ __forceinline__ float4 load_stream_f4(const void* p) {
   const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
   return make_float4(v.x, v.y, v.z, v.w);
 }
-
-__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // fp32 -> bf16 bits, round to nearest even (gfx950 converts in hardware,
 // v_cvt_pk_bf16_f32); NaN stays NaN.
@@ -39,83 +36,94 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// Data-parallel-primitive moves within 16-lane rows (gfx9 DPP controls).
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
-}
-constexpr int kDppXor1 = 0xB1;       // quad_perm [1,0,3,2]
-constexpr int kDppXor2 = 0x4E;       // quad_perm [2,3,0,1]
-constexpr int kDppRor4 = 0x124;      // row_ror:4
-constexpr int kDppRor8 = 0x128;      // row_ror:8
-constexpr int kDppHalfMirror = 0x141;
-
-// Sum over groups of LANES consecutive lanes (8 or 16); every lane of the
-// group receives the group's sum.
-template <int LANES>
-__device__ __forceinline__ float group_sum(float x) {
-  if constexpr (LANES == 16) {
-    x += dpp<kDppRor8>(x);
-    x += dpp<kDppRor4>(x);
-  } else {
-    static_assert(LANES == 8, "group of 8 or 16 lanes");
-    x += dpp<kDppHalfMirror>(x);
-  }
-  x += dpp<kDppXor1>(x);
-  x += dpp<kDppXor2>(x);
-  return x;
-}
-
 __device__ __forceinline__ float shfl_xor(float x, int m) { return __shfl_xor(x, m, 64); }
 
 __device__ __forceinline__ void raise_error(uint32_t* err, uint32_t bit) {
   atomicOr(err, bit);
 }
 
-// Store one row's result: the final output (splits == 1) or an fp32 partial.
-// `vals` holds NV consecutive head-dim values starting at d0.
-template <int NV>
-__device__ __forceinline__ void store_row_values(const AttnArgs& a, int dtype, int pair, int z,
-                                                 int s, int i, int d0, const float* vals) {
-  const int r = z * a.rb + i;
-  if (a.splits > 1) {
-    size_t base = ((((size_t)pair * a.n_rb + z) * a.splits + s) * a.rb + i) * a.D + d0;
-    float* dst = a.o_part + base;
-#pragma unroll
-    for (int e = 0; e < NV; e += 4)
-      *reinterpret_cast<float4*>(dst + e) = make_float4(vals[e], vals[e + 1], vals[e + 2], vals[e + 3]);
-    return;
-  }
-  const int b = pair / a.Hkv, g = pair % a.Hkv;
-  const int t = r / a.G, hh = r % a.G;
-  size_t o = (((size_t)b * a.T + t) * a.Hq + g * a.G + hh) * a.D + d0;
-  if (dtype == SPEC_BF16) {
-    uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) + o;
-#pragma unroll
-    for (int e = 0; e < NV; e += 4) {
-      uint2 w = make_uint2(pack_bf16x2(vals[e], vals[e + 1]), pack_bf16x2(vals[e + 2], vals[e + 3]));
-      *reinterpret_cast<uint2*>(dst + e) = w;
-    }
-  } else {
-    float* dst = reinterpret_cast<float*>(a.out) + o;
-#pragma unroll
-    for (int e = 0; e < NV; e += 4)
-      *reinterpret_cast<float4*>(dst + e) = make_float4(vals[e], vals[e + 1], vals[e + 2], vals[e + 3]);
-  }
+// LDS byte address of a __shared__ object (the value M0 takes for a copy).
+template <typename T>
+__device__ __forceinline__ uint32_t lds_addr(T* p) {
+  return (uint32_t)(uintptr_t)SPEC_LDS(T, p);
 }
 
-// Store one row's log2-domain sum-exp (partial) or natural-log lse (final).
-__device__ __forceinline__ void store_row_lse(const AttnArgs& a, int pair, int z, int s, int i,
-                                              float lse2) {
-  const int r = z * a.rb + i;
-  if (a.splits > 1) {
-    a.lse_part[(((size_t)pair * a.n_rb + z) * a.splits + s) * a.rb + i] = lse2;
-    return;
+// Direct 16-byte-per-lane copy global -> LDS (global_load_lds_dwordx4).
+// Lane i's 16 bytes land at LDS address m0 + 16 * i; m0 must be wave-uniform.
+// Issued through inline assembly so that the compiler does not insert a
+// full memory-counter wait before every LDS read: the kernels that use it
+// count their copies themselves and wait with wait_vm<N>().
+__device__ __forceinline__ void copy16_to_lds(const void* gaddr, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gaddr), "s"(m0)
+               : "memory", "m0");
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight
+// (gfx9 s_waitcnt encoding; expcnt and lgkmcnt left unconstrained).
+// Inline assembly with a memory clobber, so that no LDS read is moved above it.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// Workgroup barrier without the memory fence __syncthreads() implies (which
+// would also wait for every copy still in flight).
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" : : : "memory"); }
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// with M[i][e] the e-th 16-bit value at lane i's address, lane l receives
+// M[4j + l/4][l%4] as its j-th value (j = 0..3).
+__device__ __forceinline__ s16x4 lds_read_tr16(uint32_t addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(SPEC_LDS(s16x4, (uintptr_t)addr));
+}
+
+// ---------------------------------------------------------------- split merge
+// Partial results cross workgroups through the workspace.  They are written
+// and read with device-coherent (sc1) buffer accesses: an sc1 store goes
+// through the XCD's L2 to the device coherence point, and an sc1 load fetches
+// from it, so no L2 write-back or invalidate (what a device-scope fence
+// costs on a multi-XCD part) is needed; a wait for the stores to complete
+// before the arrival atomic orders them.
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+constexpr int kSc1 = 16;                     // cache-policy bit SC1 of buffer accesses
+constexpr int32_t kRsrcWord3 = 0x00020000;   // raw 32-bit buffer (gfx9 descriptor word 3)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcWord3);
+}
+__device__ __forceinline__ void store_sc1_f4(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, off, 0, kSc1);
+}
+__device__ __forceinline__ void store_sc1_f1(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int32_t, v), r, off, 0, kSc1);
+}
+__device__ __forceinline__ f32x4 load_sc1_f4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSc1));
+}
+__device__ __forceinline__ float load_sc1_f1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kSc1));
+}
+
+// Arrival at the end of a split: returns true (in every thread of the
+// workgroup) iff this workgroup is the last of `splits` to arrive on
+// `counter`; that workgroup resets the counter to zero and may then read,
+// with sc1 loads, what the others wrote with sc1 stores before arriving.
+__device__ __forceinline__ bool arrive_last(uint32_t* counter, int splits) {
+  __shared__ int s_last;
+  wait_vm<0>();      // this thread's sc1 stores have reached the coherence point
+  __syncthreads();   // ... and every other thread's
+  if (threadIdx.x == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = prev + 1 == (uint32_t)splits;
+    if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = last ? 1 : 0;
   }
-  if (a.lse == nullptr) return;
-  const int b = pair / a.Hkv, g = pair % a.Hkv;
-  const int t = r / a.G, hh = r % a.G;
-  a.lse[((size_t)b * a.T + t) * a.Hq + g * a.G + hh] = lse2 * kLn2;
+  __syncthreads();
+  return s_last != 0;
 }
 
 }  // namespace spec

@@ -6,7 +6,7 @@
 // M = max_s x_s, and lse = (M + log2 sum_s 2^(x_s - M)) * ln 2.  This is the
 // exact softmax over the union of the splits' keys.
 //
-// The fp32 kernel is the plain path for fp32 inputs (one wavefront per query
+// The fp32 kernels are the plain path for fp32 inputs (one wavefront per query
 // row and split; lanes take one key each for q.k, then the head dimension for
 // P.V).  It serves the draft view (window or budget list) and the tree verify
 // with the same definitions as the bf16 kernels.
@@ -239,6 +239,73 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
     if (D > 64) out[lane + 64] = o1;
     if (lane == 0 && a.lse != nullptr) a.lse[oi] = lse2 * kLn2;
   }
+}
+
+// ------------------------------------------------------------------ fp32 verify prep
+// One block per sequence: validates cache_len and parents, builds each
+// node's ancestor-or-self bitmask, and writes the remapped positions
+// (non-padding slots before cache_len, plus the node's depth).
+__global__ __launch_bounds__(256) void verify_prep_kernel(
+    int N, int capacity, const int32_t* __restrict__ cache_len, const uint8_t* __restrict__ pad,
+    int64_t pad_sb, const int32_t* __restrict__ parents, int64_t par_sb, int32_t* pos_ids,
+    uint64_t* anc_ws, int32_t* bad_ws, uint32_t* err) {
+  const int b = blockIdx.x, tid = threadIdx.x;
+  __shared__ int par_s[kMaxNodes];
+  __shared__ int cnt_s[4];
+  const int L = cache_len[b];
+  const bool bad_len = L < 0 || L > capacity;
+  bool bad_par = false;
+  if (tid < N) {
+    const int p = parents[b * par_sb + tid];
+    par_s[tid] = p;
+    bad_par = !(p >= -1 && p < tid);
+  }
+  const bool any_bad_par = __syncthreads_or(bad_par);
+
+  int cnt = 0;
+  if (pad != nullptr && pos_ids != nullptr && !bad_len) {
+    const uint8_t* row = pad + b * pad_sb;
+    for (int j = tid * 4; j < L; j += 256 * 4) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(row + j);
+      const int nb = min(4, L - j);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) cnt += (e < nb) && ((w >> (8 * e)) & 0xffu);
+    }
+  }
+#pragma unroll
+  for (int msk = 32; msk >= 1; msk >>= 1) cnt += __shfl_xor(cnt, msk, 64);
+  if ((tid & 63) == 0) cnt_s[tid >> 6] = cnt;
+  __syncthreads();
+
+  const int n_pad = cnt_s[0] + cnt_s[1] + cnt_s[2] + cnt_s[3];
+  const bool bad = bad_len || any_bad_par;
+  if (tid == 0) {
+    if (bad_len) raise_error(err, SPEC_DEV_CACHE_LEN);
+    if (any_bad_par) raise_error(err, SPEC_DEV_PARENT);
+    bad_ws[b] = bad ? 1 : 0;
+  }
+  if (tid < N) {
+    // walk to the root: parents precede children, so this ends
+    uint64_t anc = 0;
+    int depth = -1;
+    if (!bad) {
+      for (int j = tid; j >= 0; j = par_s[j]) {
+        anc |= 1ull << j;
+        ++depth;
+      }
+    }
+    anc_ws[(size_t)b * N + tid] = anc;
+    if (pos_ids != nullptr) pos_ids[(size_t)b * N + tid] = bad ? -1 : (L - n_pad) + depth;
+  }
+}
+
+hipError_t launch_verify_prep(const AttnArgs& a, const int32_t* parents, int64_t parents_sb,
+                              int32_t* pos_ids, uint64_t* anc_ws, int32_t* bad_ws,
+                              hipStream_t st) {
+  hipLaunchKernelGGL(verify_prep_kernel, dim3(a.B), dim3(256), 0, st, a.T, a.capacity,
+                     a.cache_len, a.pad, a.pad_sb, parents, parents_sb, pos_ids, anc_ws,
+                     bad_ws, a.err);
+  return hipGetLastError();
 }
 
 hipError_t launch_attn_f32(const AttnArgs& a, int mode, hipStream_t st) {

@@ -1,13 +1,14 @@
 // Internal declarations shared by the HIP sources of libspecattn (gfx950).
 //
-// Work decomposition (all three attention kernels): a "pair" is one
-// (sequence b, KV head g).  The query rows that read that KV head are
-// r = t*G + hh (draft: query t, head g*G+hh) or r = i*G + hh (verify: node i).
-// Rows are cut into row blocks of `rb` rows and the key sequence of a pair
-// into `splits` contiguous chunks of `chunk` keys (split-K flash-decode).
-// Each (pair, row block, split) is one wavefront; it writes an fp32 partial
-// (o normalised by its own softmax sum, and its log2-domain sum-exp) that the
-// combine kernel merges.  With a single split the wavefront writes the final
+// Work decomposition of the attention kernels: a "pair" is one (sequence b,
+// KV head g).  The query rows that read that KV head are r = t*G + hh (draft:
+// query t, head g*G+hh) or r = i*G + hh (verify: tree node i).  A pair's rows
+// are cut into row blocks and its key sequence into `splits` contiguous
+// ranges of 32-key tiles (split-K flash-decode).  One workgroup handles one
+// (pair, row block, split) and writes an fp32 partial: o normalised by its own
+// softmax sum and the log2-domain sum-exp.  The workgroup that finishes a
+// (pair, row block) last merges the partials into the final output, so every
+// call is a single kernel launch.  With one split the workgroup writes the
 // output directly.
 #pragma once
 
@@ -23,10 +24,15 @@ constexpr size_t kHeaderBytes = 256;           // [0,4): device error word
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr int kMaxNodes = 64;                  // one uint64 ancestor mask per node
+constexpr int kTileKeys = 32;                  // keys per KV tile
+constexpr int kMaxGatherKeys = 2048;           // budget indices one workgroup stages in LDS
+constexpr int kMaxPadWords = 1024;             // 32-key pad words one workgroup stages in LDS
+constexpr int kMergeFan = 8;                   // partials one split-merge step reads
+constexpr int kMaxSplits = kMergeFan * kMergeFan;
 
 enum Mode : int { kDraftWindow = 0, kDraftGather = 1, kVerify = 2 };
 
-// Everything a wavefront of an attention kernel needs, passed by value.
+// Everything a workgroup of an attention kernel needs, passed by value.
 struct AttnArgs {
   // tensors
   const void* q;          // [B][T][Hq][D]
@@ -49,59 +55,48 @@ struct AttnArgs {
   const void* tk;
   const void* tv;
   int64_t tkb, tkh, tkt;
-  const uint64_t* anc;    // [B][N] ancestor-or-self masks (workspace)
-  const int32_t* bad;     // [B] nonzero = sequence rejected by the prep kernel
+  const int32_t* parents;
+  int64_t par_sb;
+  int32_t* pos_ids;
+  const uint64_t* anc;    // fp32 path: [B][N] ancestor-or-self masks (workspace)
+  const int32_t* bad;     // fp32 path: [B] nonzero = sequence rejected by the prep kernel
   // decomposition
-  int32_t rb, n_rb, splits, chunk;
+  int32_t rb, n_rb, splits;
+  int32_t chunk;          // fp32 path: keys per split
+  int32_t tps;            // bf16 path: tiles per split
+  int32_t units;          // bf16 path: pairs * splits
   // outputs
   float* o_part;          // [pair][n_rb][splits][rb][D]
   float* lse_part;        // [pair][n_rb][splits][rb]   (log2 domain)
-  void* out;              // final output when splits == 1
+  float* o_part1;         // bf16 path: [pair][n_rb][n_blk][rb][D] block merges
+  float* lse_part1;       // bf16 path: [pair][n_rb][n_blk][rb]
+  int32_t n_blk;          // bf16 path: ceil(splits / kMergeFan)
+  uint32_t* cnt_l0;       // [pair][n_rb][n_blk] arrival counters (zero between calls)
+  uint32_t* cnt_l1;       // [pair][n_rb]
+  uint32_t* cnt_pos;      // [B][2] pad-count arrival (verify positions)
+  void* out;              // final output
   float* lse;             // final lse (natural log) or null
   uint32_t* err;          // device error word
 };
 
 struct Plan {
-  int32_t rows = 0, rb = 0, n_rb = 0, splits = 0, chunk = 0;
-  size_t o_off = 0, lse_off = 0, anc_off = 0, bad_off = 0, total = 0;
+  int32_t rows = 0, rb = 0, n_rb = 0, splits = 0, chunk = 0, tps = 0;
+  int32_t rt = 0, wk = 0;   // bf16 kernel shape: 16-row MFMA tiles per wave, key groups
+  size_t cnt_off = 0, o_off = 0, lse_off = 0, o1_off = 0, lse1_off = 0, anc_off = 0, bad_off = 0,
+         total = 0;
+  int32_t n_blk = 1;
 };
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Split-K plan: enough wavefronts to keep 256 CUs busy, at least `min_keys`
-// keys per split, chunk a multiple of `tile`.
-inline void plan_splits(Plan& p, int64_t pairs, int64_t keys, int64_t min_keys, int64_t tile,
-                        int64_t target_waves) {
-  if (keys < 1) keys = 1;
-  int64_t units = pairs * p.n_rb;
-  int64_t s = cdiv(target_waves, units > 0 ? units : 1);
-  int64_t smax = cdiv(keys, min_keys);
-  if (s > smax) s = smax;
-  if (s < 1) s = 1;
-  int64_t chunk = cdiv(cdiv(keys, s), tile) * tile;
-  p.chunk = (int32_t)chunk;
-  p.splits = (int32_t)cdiv(keys, chunk);
-}
-
-inline void plan_partials(Plan& p, int64_t pairs, int D) {
-  size_t off = kHeaderBytes;
-  if (p.splits > 1) {
-    size_t n = (size_t)pairs * p.n_rb * p.splits * p.rb;
-    p.o_off = off;
-    off = align_up(off + n * D * sizeof(float), 256);
-    p.lse_off = off;
-    off = align_up(off + n * sizeof(float), 256);
-  }
-  p.total = off;
-}
-
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error; arguments were validated.
-hipError_t launch_draft(const AttnArgs& a, int dtype, hipStream_t st);
-hipError_t launch_verify(const AttnArgs& a, int dtype, const int32_t* parents,
-                         int64_t parents_sb, int32_t* pos_ids, uint64_t* anc_ws,
-                         int32_t* bad_ws, hipStream_t st);
+hipError_t launch_attn_bf16(const AttnArgs& a, int mode, const Plan& p, hipStream_t st);
+hipError_t launch_verify_prep(const AttnArgs& a, const int32_t* parents, int64_t parents_sb,
+                              int32_t* pos_ids, uint64_t* anc_ws, int32_t* bad_ws,
+                              hipStream_t st);
+hipError_t launch_attn_f32(const AttnArgs& a, int mode, hipStream_t st);
 hipError_t launch_combine(const AttnArgs& a, int dtype, hipStream_t st);
 hipError_t launch_accept(int B, int N, int V, const float* logits, const int32_t* tokens,
                          const int32_t* parents, int64_t parents_sb, int max_depth,
