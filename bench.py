@@ -320,6 +320,61 @@ def cpu_baseline(layers, torch, budget_s=12.0):
                 seconds=elapsed)
 
 
+# ------------------------------------------------------------ HBM traffic
+
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+TRAFFIC_PROFILE = os.path.join(PROFILE_DIR, "verify_chain3_1m_hbm_traffic.md")
+
+
+TRAFFIC_SOURCES = ("attn.hip", "api.hip", "dev_common.h", "spec_internal.h")
+
+
+def source_digest():
+    """sha256 over the sources of the verify kernel and of its launch plan,
+    so that counter figures taken on other kernel code are never reported."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in TRAFFIC_SOURCES:
+        h.update(name.encode())
+        with open(os.path.join(ROOT, "sparse_kv_attention_sink_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per verify launch from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, each scaled by the same counter's reading for a
+    plain copy of known size), or None if it is missing or was taken on other
+    kernel sources."""
+    try:
+        with open(TRAFFIC_PROFILE) as f:
+            text = f.read()
+    except OSError:
+        return None
+    fields = {}
+    for line in text.splitlines():
+        line = line.strip().lstrip("-").strip()
+        if ":" in line and line.split(":", 1)[0] in ("source_sha256", "traffic_bytes_per_launch"):
+            k, v = line.split(":", 1)
+            fields[k] = v.strip().strip("`")
+    if fields.get("source_sha256") != source_digest() or "traffic_bytes_per_launch" not in fields:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
+def copy_probe(torch, gib=1, reps=4):
+    """A plain device copy of known size, the calibration of the HBM byte
+    counters: FETCH_SIZE and WRITE_SIZE of one dispatch of it should read
+    gib GiB each."""
+    n = gib << 30
+    x = torch.ones(n // 2, dtype=torch.bfloat16, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(reps):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "dispatches": reps}))
+
+
 # ------------------------------------------------------------ main
 
 def main():
@@ -329,7 +384,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--layers", type=int, default=LAYERS)
     ap.add_argument("--skip-16k", action="store_true")
+    ap.add_argument("--skip-1m", action="store_true",
+                    help="only the 16K batch-8 sweep (for profiling it alone)")
     ap.add_argument("--skip-cpu", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a 1 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only: the hot path needs no "
@@ -339,7 +398,13 @@ def main():
     import sparse_kv_attention_sink_amd as skg
     skg.load()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_probe:
+        copy_probe(torch)
+        return
 
+    if args.skip_1m:
+        print(json.dumps({"ctx16k": run_16k(args, torch, skg)}), flush=True)
+        return
     r1m, layers = run_1m(args, torch, skg)
     log(f"[bench] 1M step: {r1m['ms_step']:.3f} ms, {r1m['gbs']:.1f} GB/s")
     cpu = None
@@ -377,7 +442,7 @@ def main():
         "call_gbs": {k: round(v, 1) for k, v in r1m["call_gbs"].items()},
         "roofline": {"kernel": "verify (chain 3 over 1,048,576 keys, 8 KV heads)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "bytes_per_launch": r1m["verify_bytes_per_launch"],
                      "avg_launch_ms": round(v_ms, 4)},
         "cpu_baseline": cpu,

@@ -87,7 +87,8 @@ enum {
 };
 
 typedef struct {
-  int32_t batch;          /* B >= 0 (0 = nothing to do) */
+  int32_t batch;          /* B >= 0; with B = 0 a call launches nothing and
+                             returns SPEC_OK (tensor pointers may be NULL) */
   int32_t n_q_heads;      /* Hq >= 1 */
   int32_t n_kv_heads;     /* Hkv >= 1, Hq % Hkv == 0 */
   int32_t head_dim;       /* D: 64 or 128 */
@@ -181,6 +182,7 @@ spec_status spec_attn_verify_tree(const spec_dims* dims, const void* q, int32_t 
  *   bonus[b]       = the target of the last accepted row (row 0 if none).
  * A path longer than max_depth raises SPEC_DEV_DEPTH (the first max_depth
  * entries are written).  1 <= N <= 64; parents as in spec_attn_verify_tree.
+ * batch >= 0; with batch = 0 nothing is launched (pointers may be NULL).
  */
 spec_status spec_accept_greedy(int32_t batch, int32_t n_nodes, int32_t vocab,
                                const float* logits, const int32_t* draft_tokens,

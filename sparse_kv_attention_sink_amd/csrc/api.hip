@@ -294,6 +294,7 @@ spec_status spec_attn_draft_sparse(const spec_dims* dims, const void* q, int32_t
   spec_status st = check_dims(dims);
   if (st != SPEC_OK) return st;
   if (n_q_tokens < 1) return fail(SPEC_E_INVALID, "n_q_tokens %d < 1", n_q_tokens);
+  if (dims->batch == 0) return SPEC_OK;   // nothing to read or write; pointers may be NULL
   if ((st = check_kv(cache, dims, "cache", true)) != SPEC_OK) return st;
   if (q == nullptr || out == nullptr || cache_len == nullptr)
     return fail(SPEC_E_INVALID, "q, out and cache_len must not be NULL");
@@ -318,7 +319,6 @@ spec_status spec_attn_draft_sparse(const spec_dims* dims, const void* q, int32_t
                 workspace == nullptr ? (size_t)0 : workspace_bytes);
   if (!aligned(workspace, 256)) return fail(SPEC_E_INVALID, "workspace must be 256-byte aligned");
   if (grid_size(dims, p) > kMaxGrid) return fail(SPEC_E_UNSUPPORTED, "problem too large for one launch");
-  if (dims->batch == 0) return SPEC_OK;
 
   AttnArgs a{};
   a.q = q;
@@ -372,6 +372,7 @@ spec_status spec_attn_verify_tree(const spec_dims* dims, const void* q, int32_t 
   if (n_nodes < 1 || n_nodes > kMaxNodes)
     return fail(n_nodes > kMaxNodes ? SPEC_E_UNSUPPORTED : SPEC_E_INVALID,
                 "n_nodes %d outside [1, 64]", n_nodes);
+  if (dims->batch == 0) return SPEC_OK;   // nothing to read or write; pointers may be NULL
   if ((st = check_kv(cache, dims, "cache", true)) != SPEC_OK) return st;
   if ((st = check_kv(tree, dims, "tree", false)) != SPEC_OK) return st;
   if (q == nullptr || out == nullptr || cache_len == nullptr || parents == nullptr)
@@ -393,7 +394,6 @@ spec_status spec_attn_verify_tree(const spec_dims* dims, const void* q, int32_t 
                 workspace == nullptr ? (size_t)0 : workspace_bytes);
   if (!aligned(workspace, 256)) return fail(SPEC_E_INVALID, "workspace must be 256-byte aligned");
   if (grid_size(dims, p) > kMaxGrid) return fail(SPEC_E_UNSUPPORTED, "problem too large for one launch");
-  if (dims->batch == 0) return SPEC_OK;
 
   AttnArgs a{};
   a.q = q;
@@ -455,6 +455,7 @@ spec_status spec_accept_greedy(int32_t batch, int32_t n_nodes, int32_t vocab, co
     return fail(n_nodes > kMaxNodes ? SPEC_E_UNSUPPORTED : SPEC_E_INVALID, "n_nodes %d outside [1, 64]", n_nodes);
   if (vocab < 1) return fail(SPEC_E_INVALID, "vocab %d < 1", vocab);
   if (max_depth < 1) return fail(SPEC_E_INVALID, "max_depth %d < 1", max_depth);
+  if (batch == 0) return SPEC_OK;   // nothing to read or write; pointers may be NULL
   if (logits == nullptr || draft_tokens == nullptr || parents == nullptr || accept_len == nullptr ||
       accept_path == nullptr || bonus == nullptr)
     return fail(SPEC_E_INVALID, "a required pointer is NULL");
@@ -472,7 +473,6 @@ spec_status spec_accept_greedy(int32_t batch, int32_t n_nodes, int32_t vocab, co
                 workspace == nullptr ? (size_t)0 : workspace_bytes);
   if (!aligned(workspace, 256)) return fail(SPEC_E_INVALID, "workspace must be 256-byte aligned");
   if (rows * vs > kMaxGrid) return fail(SPEC_E_UNSUPPORTED, "problem too large for one launch");
-  if (batch == 0) return SPEC_OK;
   hipError_t e = launch_accept(batch, n_nodes, vocab, logits, draft_tokens, parents, parents_stride_b,
                                max_depth, accept_len, accept_path, bonus, workspace, vs,
                                static_cast<hipStream_t>(stream), static_cast<uint32_t*>(workspace));

@@ -1,0 +1,177 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times, on sampled (sequence, KV head) pairs the oracle computes one
+by one: the million-token layer (chain-3 verify over 1,048,576 keys, the
+3-query context draft and the single-query draft over sink 4 + window 4096)
+and the ragged batch of 16 sequences with 44- and 64-node trees and padding.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import synth.device_gen as dg
+from helpers import assert_close, assert_lse_close, host64
+
+pytestmark = pytest.mark.gpu
+
+skg = pytest.importorskip("sparse_kv_attention_sink_amd")
+
+G = 4
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    skg.load()
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    """bf16 device tensor -> uint16 bit patterns on the host."""
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def verify_pair_ref(d, b, g, cache_len_b, parents, pad=None):
+    """Oracle verify of one (sequence, KV head) pair, as a one-sequence,
+    one-KV-head problem."""
+    q = bits(d["verify_q"][b:b + 1, :, g * G:(g + 1) * G])
+    k = bits(d["k"][b:b + 1, g:g + 1, :cache_len_b])
+    v = bits(d["v"][b:b + 1, g:g + 1, :cache_len_b])
+    tk = bits(d["tree_k"][b:b + 1, g:g + 1])
+    tv = bits(d["tree_v"][b:b + 1, g:g + 1])
+    padb = None if pad is None else pad[b:b + 1, :cache_len_b]
+    return oracle.verify_attn_ref(q, k, v, np.array([cache_len_b]), tk, tv, parents,
+                                  scale=1 / math.sqrt(128), pad=padb)
+
+
+# ------------------------------------------------------------ 1M layer
+
+@pytest.fixture(scope="module")
+def layer1m():
+    d = dg.layer_1m(0)
+    torch.cuda.synchronize()
+    yield d
+    del d
+    torch.cuda.empty_cache()
+
+
+L1M = 1 << 20
+
+
+def test_1m_verify_chain3_sampled(layer1m):
+    d = layer1m
+    dims = skg.make_dims(1, 32, 8, 128, skg.SPEC_BF16)
+    ws = skg.new_workspace(skg.verify_workspace_bytes(dims, 3, L1M), "cuda")
+    cl = torch.tensor([L1M], dtype=torch.int32, device="cuda")
+    par = torch.tensor([-1, 0, 1], dtype=torch.int32, device="cuda")
+    out, lse, pos = skg.spec_attn_verify_tree(d["verify_q"], d["k"], d["v"], cl, d["tree_k"],
+                                              d["tree_v"], par, workspace=ws)
+    torch.cuda.synchronize()
+    assert skg.spec_device_status(ws) == 0
+    got = host64(out)
+    lse = lse.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got))
+    np.testing.assert_array_equal(pos.cpu().numpy(), [[L1M, L1M + 1, L1M + 2]])
+    for g in (0, 5):
+        ref, lse_ref = verify_pair_ref(d, 0, g, L1M, np.array([-1, 0, 1]))
+        assert_close(got[:, :, g * G:(g + 1) * G], ref, "bf16", f"1M verify kv head {g}")
+        assert_lse_close(lse[:, :, g * G:(g + 1) * G], lse_ref, 1e-3, "1M verify lse")
+
+
+@pytest.mark.parametrize("which", ["ctx", "fwd"])
+def test_1m_window_draft_sampled(layer1m, which):
+    d = layer1m
+    q = d["ctx_q"] if which == "ctx" else d["fwd_q"][1]
+    T = q.shape[1]
+    dims = skg.make_dims(1, 32, 8, 128, skg.SPEC_BF16)
+    ws = skg.new_workspace(skg.draft_workspace_bytes(dims, T, 4 + 4096 + T - 1), "cuda")
+    cl = torch.tensor([L1M], dtype=torch.int32, device="cuda")
+    out, lse = skg.spec_attn_draft_sparse(q, d["k"], d["v"], cl, n_sink=4, window=4096,
+                                          workspace=ws)
+    torch.cuda.synchronize()
+    assert skg.spec_device_status(ws) == 0
+    got = host64(out)
+    lse = lse.cpu().numpy().astype(np.float64)
+    lo = L1M - T + 1 - 4096
+    for g in (2, 7):
+        # the oracle sees the sink rows and the window rows, re-indexed into
+        # one compact cache whose length keeps the queries' positions
+        keep = torch.cat([torch.arange(4), torch.arange(lo, L1M)]).cuda()
+        kk = bits(d["k"][0, g].index_select(0, keep))[None, None]
+        vv = bits(d["v"][0, g].index_select(0, keep))[None, None]
+        qq = bits(q[:, :, g * G:(g + 1) * G])
+        ref, lse_ref = oracle.draft_attn_ref(qq, kk, vv, np.array([len(keep)]),
+                                             scale=1 / math.sqrt(128), n_sink=4, window=4096)
+        assert_close(got[:, :, g * G:(g + 1) * G], ref, "bf16", f"1M {which} draft head {g}")
+        assert_lse_close(lse[:, :, g * G:(g + 1) * G], lse_ref, 1e-3, "1M draft lse")
+
+
+# ------------------------------------------------------------ ragged batch
+
+@pytest.fixture(scope="module", params=[(10, 14, 12, 8), (10, 18, 18, 18)],
+                ids=["tree44", "tree64"])
+def ragged(request):
+    d = dg.ragged_batch(request.param)
+    torch.cuda.synchronize()
+    yield d
+    del d
+    torch.cuda.empty_cache()
+
+
+def test_ragged_verify_sampled(ragged):
+    d = ragged
+    B, N = len(d["lens"]), d["tree"].n
+    cl = torch.from_numpy(d["lens"]).cuda()
+    pad = torch.from_numpy(d["pad"]).cuda()
+    par = torch.from_numpy(d["tree"].parents).cuda()
+    out, lse, pos = skg.spec_attn_verify_tree(d["verify_q"], d["k"], d["v"], cl, d["tree_k"],
+                                              d["tree_v"], par, pad=pad)
+    torch.cuda.synchronize()
+    got = host64(out)
+    lse = lse.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got))
+    np.testing.assert_array_equal(pos.cpu().numpy(),
+                                  oracle.position_ids(d["lens"], d["pad"], d["tree"].parents))
+    longest = int(np.argmax(d["lens"]))
+    for b, g in [(0, 0), (longest, 3), (B - 1, 7)]:
+        ref, lse_ref = verify_pair_ref(d, b, g, int(d["lens"][b]), d["tree"].parents, d["pad"])
+        sl = (slice(b, b + 1), slice(None), slice(g * G, (g + 1) * G))
+        assert_close(got[sl], ref, "bf16", f"ragged verify N={N} pair ({b}, {g})")
+        assert_lse_close(lse[sl], lse_ref, 1e-3, "ragged verify lse")
+
+
+def test_ragged_accept(ragged):
+    tree = ragged["tree"]
+    a = synth.make_accept_case(synth.SEEDS[5] + tree.n, tree, 16, 128256)
+    got = skg.spec_accept_greedy(torch.from_numpy(a.logits).cuda(),
+                                 torch.from_numpy(a.tokens).cuda(),
+                                 torch.from_numpy(a.parents).cuda(), a.max_depth)
+    torch.cuda.synchronize()
+    ref = oracle.accept_ref(a.logits, a.tokens, a.parents, a.max_depth)
+    for x, r in zip(got, ref):
+        np.testing.assert_array_equal(x.cpu().numpy(), r)
+    np.testing.assert_array_equal(got[0].cpu().numpy(), a.expected_len)
+
+
+def test_ragged_verify_peaked_sampled():
+    """Peaked variant: N(0, 1) keys and values, queries 4 N(0, 1), so scores
+    spread by about 4, a few keys carry most of each softmax and the outputs
+    are far from the near-zero averages of the scaled workload."""
+    d = dg.ragged_batch((10, 18, 18, 18), B=4, lo=2048, hi=8192, value_scale=1.0, q_scale=4.0,
+                        seed=synth.SEEDS[5] + 99)
+    cl = torch.from_numpy(d["lens"]).cuda()
+    pad = torch.from_numpy(d["pad"]).cuda()
+    par = torch.from_numpy(d["tree"].parents).cuda()
+    out, lse, _ = skg.spec_attn_verify_tree(d["verify_q"], d["k"], d["v"], cl, d["tree_k"],
+                                            d["tree_v"], par, pad=pad)
+    torch.cuda.synchronize()
+    got = host64(out)
+    for b, g in [(0, 1), (3, 6)]:
+        ref, _ = verify_pair_ref(d, b, g, int(d["lens"][b]), d["tree"].parents, d["pad"])
+        mag = np.abs(ref[~np.isnan(ref)]).max()
+        assert mag > 0.5
+        assert_close(got[b:b + 1, :, g * G:(g + 1) * G], ref, "bf16", f"peaked pair ({b}, {g})",
+                     magnitude=mag)
