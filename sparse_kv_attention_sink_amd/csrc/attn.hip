@@ -157,7 +157,7 @@ __device__ __forceinline__ void issue_tile(KeySrc ks, int t, uint32_t stage, int
     const uint32_t m0 = __builtin_amdgcn_readfirstlane(stage + region * Ge::KB + ii * 1024);
     if (contig) {
       const char* sb = seg + (size_t)(j0 + ii * Ge::RPI) * rowb;   // wave-uniform
-      copy16_to_lds(sb + ((uint32_t)rl * rowb + col), m0);
+      copy16_to_lds_s(sb, (uint32_t)rl * rowb + col, m0);
     } else {
       const int j = tile_row<MODE>(ks, t, r);
       copy16_to_lds(seg + ((uint32_t)j * rowb + col), m0);
@@ -488,17 +488,63 @@ void attn_bf16_kernel(AttnArgs a) {
   const int wl = WK == 1 ? wave : 0;   // index of this wavefront among the loaders
 
   // ---------------------------------------------------------------- main loop
+  // m starts at a finite stand-in for -inf: the first visible score of a row
+  // then gives exp2(score - m) = +inf, which the growth test catches, while a
+  // masked score (-inf) still gives 0 instead of the NaN of -inf - (-inf).
+  constexpr float kNoMax = -1e30f;
   f32x4 acc[RT][NDT];
   float m[RT], lsum[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    m[rt] = -INFINITY;
+    m[rt] = kNoMax;
     lsum[rt] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) acc[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const float c2 = a.scale_log2;
   const bool row_masks = MODE != kVerify && T > 1;
+
+  // LDS read addresses of this lane within stage 0 (loop invariant; the stage
+  // and the second 16-key half are immediate offsets): K fragment chunk cc of
+  // key row l16, and the V^T transpose read of d tile dt for keys 4*q4 + j.
+  // Rows r and r + 16 share their swizzle.
+  uint32_t koff[ND], voff[NDT];
+#pragma unroll
+  for (int cc = 0; cc < ND; ++cc)
+    koff[cc] = ring_base + l16 * ROWB + (((cc * 4 + q4) ^ swz_k<D>(l16)) * 16);
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    const int r = 4 * q4 + (l16 >> 2);
+    const int byte = (dt * 16 + 4 * (l16 & 3)) * 2;
+    voff[dt] = ring_base + KB + r * ROWB + (((byte >> 4) ^ swz_v<D>(r)) << 4) + (byte & 15);
+  }
+
+  // Copies of a contiguous cache tile: this wavefront's DPW pieces all lie in
+  // one region (K or V) and cover rows ii0*RPI .. of the tile, so one scalar
+  // base per tile plus loop-invariant lane offsets address them.
+  static_assert(WK != 1 || (Ge::DPT / 2) % DPW == 0, "a wavefront's pieces stay in one region");
+  const int region = (wl * DPW) / (Ge::DPT / 2), ii0 = (wl * DPW) % (Ge::DPT / 2);
+  const char* cbase = region ? ks.v : ks.k;
+  const uint32_t m0w = ring_base + region * KB + ii0 * 1024;
+  uint32_t vo[DPW];
+#pragma unroll
+  for (int u = 0; u < DPW; ++u) {
+    const int rl = lane / CH, r = (ii0 + u) * RPI + rl;
+    vo[u] = (uint32_t)((u * RPI + rl) * ks.rowb) +
+            (uint32_t)(((lane % CH) ^ (region ? swz_v<D>(r) : swz_k<D>(r))) * 16);
+  }
+  // Issue tile tn into stage sn (WK = 1).
+  auto issue = [&](int tn, int sn) __attribute__((always_inline)) {
+    const int j0 = is_tree_tile(ks, tn, MODE) ? -1 : tile_first_row<MODE>(ks, tn);
+    if (j0 >= 0) {
+      const char* base = cbase + (size_t)(j0 + ii0 * RPI) * ks.rowb;
+#pragma unroll
+      for (int u = 0; u < DPW; ++u)
+        copy16_to_lds_s(base, vo[u], (uint32_t)(m0w + sn * SB + u * 1024));
+    } else {
+      issue_tile<MODE, D, DPW>(ks, tn, ring_base + sn * SB, wl, lane);
+    }
+  };
 
   // Nothing but ring copies may be in flight from here on.  The wait is the
   // compiler's own intrinsic, so it knows the query loads are complete and
@@ -509,169 +555,180 @@ void attn_bf16_kernel(AttnArgs a) {
   if constexpr (WK == 1) {
 #pragma unroll
     for (int u = 0; u < NS - 1; ++u)
-      if (k0 + u < k1) issue_tile<MODE, D, DPW>(ks, k0 + u, ring_base + u * SB, wl, lane);
+      if (k0 + u < k1) issue(k0 + u, u);
   } else {
     if (k0 < k1) load_tile_regs<MODE, D>(ks, k0, lane, stg);
   }
 
-  for (int t = k0; t < k1; ++t) {
-    const int i = t - k0;
-    uint32_t sb;
-    if constexpr (WK == 1) {
-      wait_tiles<DPW, NS - 2>(k1 - 1 - t);
-      barrier_only();   // every wave's copies of tile t landed; tile t-1 is consumed
-      if (t + NS - 1 < k1) issue_tile<MODE, D, DPW>(ks, t + NS - 1, ring_base + ((i + NS - 1) % NS) * SB, wl, lane);
-      sb = ring_base + (i % NS) * SB;
-    } else {
-      // the wave's own stage: LDS operations of a wave execute in order, so
-      // these writes land after the previous tile's reads and before this
-      // tile's; the next tile's loads are in flight while this one is used
-      sb = ring_base;
-      store_tile_lds<D>(sb, lane, stg);
-      if (t + 1 < k1) load_tile_regs<MODE, D>(ks, t + 1, lane, stg);
-    }
-    const bool tree_tile = MODE == kVerify && t >= cache_tiles;
-
-    // K fragments (A operand of S^T): key h*16 + l16, head-dim chunk cc*4 + q4
-    bf16x8 kf[2][ND];
+  // Unrolled by the ring depth, so that a tile's stage is a constant.
+  for (int tb = k0; tb < k1; tb += NS) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int r = h * 16 + l16;
-#pragma unroll
-      for (int cc = 0; cc < ND; ++cc)
-        kf[h][cc] = lds_load_b128(sb + r * ROWB + (((cc * 4 + q4) ^ swz_k<D>(r)) * 16));
-    }
-    f32x4 sc[RT][2];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int cc = 0; cc < ND; ++cc)
-          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[h][cc], qf[rt][cc], c, 0, 0, 0);
-        sc[rt][h] = c;
+    for (int st = 0; st < NS; ++st) {
+      const int t = tb + st;
+      if (t >= k1) break;
+      uint32_t so;   // stage offset
+      if constexpr (WK == 1) {
+        wait_tiles<DPW, NS - 2>(k1 - 1 - t);
+        barrier_only();   // every wave's copies of tile t landed; tile t-1 is consumed
+        if (t + NS - 1 < k1) issue(t + NS - 1, (st + NS - 1) % NS);
+        so = st * SB;
+      } else {
+        // the wave's own stage: LDS operations of a wave execute in order, so
+        // these writes land after the previous tile's reads and before this
+        // tile's; the next tile's loads are in flight while this one is used
+        so = 0;
+        store_tile_lds<D>(ring_base, lane, stg);
+        if (t + 1 < k1) load_tile_regs<MODE, D>(ks, t + 1, lane, stg);
       }
+      const bool tree_tile = MODE == kVerify && t >= cache_tiles;
+      // This tile's pad word (verify), read before the fragment reads so that
+      // waiting for it never waits for them; it is uniform, so the visibility
+      // test below is a scalar branch.
+      uint32_t pw = 0u;
+      if constexpr (MODE == kVerify) {
+        if (!tree_tile && a.pad != nullptr) pw = __builtin_amdgcn_readfirstlane(padbits_s[t - t0]);
+      }
+      const bool full = !tree_tile && (t + 1) * kTileKeys <= n_view && !row_masks && pw == 0u;
 
-    // Visibility of this lane's 8 keys, local index e = h*4 + i, tile key
-    // h*16 + q4*4 + i.  `full` tiles (every key visible to every row) skip it.
-    uint32_t kmask = 0xffu;
-    bool full = !tree_tile && (t + 1) * kTileKeys <= n_view && !row_masks;
-    if constexpr (MODE == kVerify) {
-      if (!tree_tile) {
-        const uint32_t pw = a.pad != nullptr ? padbits_s[t - t0] : 0u;
-        full = full && pw == 0u;
-        if (!full) {
+      // K fragments (A operand of S^T): key h*16 + l16, head-dim chunk cc*4 + q4;
+      // V^T fragments (A operand of O^T) for every d tile, read now so that
+      // their latency hides behind the scores and the softmax.
+      bf16x8 kf[2][ND], vf[NDT];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int cc = 0; cc < ND; ++cc) kf[h][cc] = lds_load_b128(koff[cc] + so + h * 16 * ROWB);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const s16x4 v0 = lds_read_tr16(voff[dt] + so);
+        const s16x4 v1 = lds_read_tr16(voff[dt] + so + 16 * ROWB);
+        vf[dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+      f32x4 sc[RT][2];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int cc = 0; cc < ND; ++cc)
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[h][cc], qf[rt][cc], c, 0, 0, 0);
+          sc[rt][h] = c;
+        }
+
+      // Visibility of this lane's 8 keys, local index e = h*4 + i, tile key
+      // h*16 + q4*4 + i.  `full` tiles (every key visible to every row) skip it.
+      uint32_t kmask = 0xffu;
+      if constexpr (MODE == kVerify) {
+        if (!tree_tile && !full) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int kk = (e >> 2) * 16 + q4 * 4 + (e & 3);
             if (t * kTileKeys + kk >= n_view || ((pw >> kk) & 1u)) kmask &= ~(1u << e);
           }
         }
-      }
-    } else if (!full) {
+      } else if (!full) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int kk = (e >> 2) * 16 + q4 * 4 + (e & 3);
-        if (t * kTileKeys + kk >= n_view) kmask &= ~(1u << e);
+        for (int e = 0; e < 8; ++e) {
+          const int kk = (e >> 2) * 16 + q4 * 4 + (e & 3);
+          if (t * kTileKeys + kk >= n_view) kmask &= ~(1u << e);
+        }
       }
-    }
-    int jpos[8];
-    if (row_masks) {
+      int jpos[8];
+      if (row_masks) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int kk = (e >> 2) * 16 + q4 * 4 + (e & 3);
-        jpos[e] = view_pos<MODE>(ks, min(t * kTileKeys + kk, n_view - 1));
+        for (int e = 0; e < 8; ++e) {
+          const int kk = (e >> 2) * 16 + q4 * 4 + (e & 3);
+          jpos[e] = view_pos<MODE>(ks, min(t * kTileKeys + kk, n_view - 1));
+        }
       }
-    }
 
-    // Scores of this lane's row in the scaled log2 domain, masked.
-    float x[RT][8], mnew[RT];
-    bool grow = false;
+      // Scores of this lane's row, masked (-inf).
+      float x[RT][8];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
+      for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[rt][e] = sc[rt][e >> 2][e & 3];
-      if (!full) {
-        uint32_t rm = kmask;
-        if (tree_tile) {
-          const uint32_t aw = (uint32_t)(ancr[rt] >> ((t - cache_tiles) * kTileKeys));
+        for (int e = 0; e < 8; ++e) x[rt][e] = sc[rt][e >> 2][e & 3];
+        if (!full) {
+          uint32_t rm = kmask;
+          if (tree_tile) {
+            const uint32_t aw = (uint32_t)(ancr[rt] >> ((t - cache_tiles) * kTileKeys));
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int kk = (e >> 2) * 16 + q4 * 4 + (e & 3);
-            if (!((aw >> kk) & 1u)) rm &= ~(1u << e);
+            for (int e = 0; e < 8; ++e) {
+              const int kk = (e >> 2) * 16 + q4 * 4 + (e & 3);
+              if (!((aw >> kk) & 1u)) rm &= ~(1u << e);
+            }
+          } else if (row_masks) {
+            const int er = erow[rt];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              bool vis = jpos[e] < er;
+              if (MODE == kDraftWindow) vis = vis && (jpos[e] < a.n_sink || jpos[e] >= er - a.window);
+              if (!vis) rm &= ~(1u << e);
+            }
           }
-        } else if (row_masks) {
-          const int er = erow[rt];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[rt][e] = ((rm >> e) & 1u) ? x[rt][e] : -INFINITY;
+        }
+      }
+
+      // p = 2^(score*c2 - m) against the running maximum m.  Lazy rescale:
+      // m is raised only when some p of the wave exceeds 2^8 (a lane's sum
+      // of p above 2^8 is the test: it holds whenever one p does), so every
+      // p used is at most 2^8, safe in fp32 and bf16; the final o = acc / l
+      // is the same either way.  The branch is wave-uniform and rare (at the
+      // first visible key of a row and when scores climb by more than 8 in
+      // log2 units), so the accumulators stay in the MFMA registers.
+      float p[RT][8], ps[RT];
+      bool grow = false;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        ps[rt] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          p[rt][e] = __builtin_amdgcn_exp2f(fmaf(x[rt][e], c2, -m[rt]));
+          ps[rt] += p[rt][e];
+        }
+        grow = grow || ps[rt] > 256.f;
+      }
+      if (__builtin_expect(__any(grow), 0)) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          float mx = x[rt][0];
+#pragma unroll
+          for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[rt][e]);
+          mx = fmaxf(mx, shfl_xor(mx, 16));
+          mx = fmaxf(mx, shfl_xor(mx, 32));
+          const float mn = fmaxf(m[rt], mx * c2);
+          const float alpha = __builtin_amdgcn_exp2f(m[rt] - mn);
+          m[rt] = mn;
+          lsum[rt] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) acc[rt][dt] *= alpha;
+          ps[rt] = 0.f;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            bool vis = jpos[e] < er;
-            if (MODE == kDraftWindow) vis = vis && (jpos[e] < a.n_sink || jpos[e] >= er - a.window);
-            if (!vis) rm &= ~(1u << e);
+            p[rt][e] = __builtin_amdgcn_exp2f(fmaf(x[rt][e], c2, -mn));
+            ps[rt] += p[rt][e];
           }
         }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[rt][e] = ((rm >> e) & 1u) ? x[rt][e] : -INFINITY;
       }
-      float mx = x[rt][0];
-#pragma unroll
-      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[rt][e]);
-      mx = fmaxf(mx, shfl_xor(mx, 16));
-      mx = fmaxf(mx, shfl_xor(mx, 32));
-      mnew[rt] = mx * c2;
-      // First visible key of the row: nothing accumulated yet, just set m.
-      if (m[rt] == -INFINITY) m[rt] = mnew[rt];
-      grow = grow || mnew[rt] > m[rt] + 8.f;
-    }
-    // Lazy rescale: keep the running maximum unless a row's new maximum
-    // exceeds it by more than 2^8 (until then p <= 256, safe in fp32 and
-    // bf16); the final o = acc / l is the same either way.  The branch is
-    // wave-uniform and rare, so the accumulators stay in the MFMA registers.
-    if (__builtin_expect(__any(grow), 0)) {
+      uint32_t pf[RT][4];
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        const bool up = mnew[rt] > m[rt] + 8.f;
-        const float alpha = up ? __builtin_amdgcn_exp2f(m[rt] - mnew[rt]) : 1.f;
-        lsum[rt] *= alpha;
+        lsum[rt] += ps[rt];
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) acc[rt][dt] *= alpha;
-        m[rt] = up ? mnew[rt] : m[rt];
+        for (int w = 0; w < 4; ++w) pf[rt][w] = pack_bf16x2(p[rt][2 * w], p[rt][2 * w + 1]);
       }
-    }
-    uint32_t pf[RT][4];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const float mb = m[rt] == -INFINITY ? 0.f : m[rt];
-      float p[8], ps = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        p[e] = __builtin_amdgcn_exp2f(fmaf(x[rt][e], c2, -mb));
-        ps += p[e];
-      }
-      lsum[rt] += ps;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) pf[rt][w] = pack_bf16x2(p[2 * w], p[2 * w + 1]);
-    }
 
-    // O^T += V^T . P^T: V^T operand by two transpose reads per 16-wide d tile
-    // (keys 4*q4 + j, then 16 + 4*q4 + j, at d = dt*16 + l16).
+      // O^T += V^T . P^T
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      uint32_t vaddr[2];
+      for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int r = 16 * h + 4 * q4 + (l16 >> 2);
-        const int byte = (dt * 16 + 4 * (l16 & 3)) * 2;
-        vaddr[h] = sb + KB + r * ROWB + (((byte >> 4) ^ swz_v<D>(r)) << 4) + (byte & 15);
-      }
-      const s16x4 v0 = lds_read_tr16(vaddr[0]);
-      const s16x4 v1 = lds_read_tr16(vaddr[1]);
-      const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(pf[rt][0], pf[rt][1], pf[rt][2], pf[rt][3]));
-        acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb, acc[rt][dt], 0, 0, 0);
-      }
+        for (int rt = 0; rt < RT; ++rt) {
+          const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(pf[rt][0], pf[rt][1], pf[rt][2], pf[rt][3]));
+          acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pb, acc[rt][dt], 0, 0, 0);
+        }
     }
   }
 

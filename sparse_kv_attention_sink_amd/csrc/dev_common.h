@@ -60,6 +60,15 @@ __device__ __forceinline__ void copy16_to_lds(const void* gaddr, uint32_t m0) {
                : "memory", "m0");
 }
 
+// The same copy from a wave-uniform base (SGPR pair) plus a 32-bit per-lane
+// byte offset: no 64-bit address arithmetic per lane.
+__device__ __forceinline__ void copy16_to_lds_s(const void* sbase, uint32_t voff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(m0)
+               : "memory", "m0");
+}
+
 // Wait until at most N vector-memory operations of this wave are in flight
 // (gfx9 s_waitcnt encoding; expcnt and lgkmcnt left unconstrained).
 // Inline assembly with a memory clobber, so that no LDS read is moved above it.
