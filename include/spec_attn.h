@@ -40,8 +40,8 @@
  *     outputs rounded to nearest-even); SPEC_F32 is a plain fp32 path.
  *   - head_dim must be 64 or 128.  Query head h reads KV head h / (Hq / Hkv).
  *   - Size limits of the bf16 path (SPEC_E_UNSUPPORTED beyond them): a
- *     draft budget of at most 131072 positions; a verify cache capacity plus
- *     N of at most 2^21 slots.
+ *     draft budget of at most 524288 positions; a verify cache capacity plus
+ *     N of at most 2^23 slots.
  *
  * Sources (page title, then the passage):
  *   [WM] "Windowed-MTP: Removing the Full-Context Draft-KV Tax at Million-Token

@@ -104,6 +104,10 @@ Plan bf16_plan(const spec_dims* d, int32_t T, int64_t tiles, bool gather, bool v
   const int64_t groups = std::max<int64_t>(1, pairs * p.n_rb);
   int64_t S = p.wk == 4 ? std::min(cdiv(kTargetWaves, groups * 4), cdiv(tiles, 4))
                         : std::min(cdiv(kTargetWorkgroups, groups), tiles);
+  // More splits than one merge step reads only when each split streams at
+  // least 32 tiles: a second merge level costs a few microseconds, which
+  // only a long split amortises.
+  S = std::min(S, std::max<int64_t>(kMergeFan, cdiv(tiles, 32)));
   int64_t lo = 1;
   if (gather) lo = std::max(lo, cdiv(tiles, kMaxGatherKeys / kTileKeys));
   if (verify) lo = std::max(lo, cdiv(tiles, kMaxPadWords));
@@ -184,8 +188,11 @@ Plan verify_plan(const spec_dims* d, int32_t N, int32_t capacity) {
   return f32_plan(d, N, std::max(capacity, 1), true);
 }
 
+// Slices per logits row: as many as keep every block resident in one round
+// (8 blocks of 256 threads per CU), so no straggler round runs alone at the
+// end, and at least 4096 values per slice.
 int accept_vsplits(int64_t rows, int64_t V) {
-  int64_t vs = cdiv(kTargetWaves, rows > 0 ? rows : 1);
+  int64_t vs = kTargetWorkgroups * 4 / (rows > 0 ? rows : 1);
   int64_t vmax = V / 4096;
   if (vmax < 1) vmax = 1;
   if (vs > vmax) vs = vmax;

@@ -362,6 +362,7 @@ void attn_bf16_kernel(AttnArgs a) {
     }
     if (leader && tid == 0 && bad_par) raise_error(a.err, SPEC_DEV_PARENT);
     bad = bad || bad_par;
+    __syncthreads();   // the masks and depths are read by every thread below
   }
 
   // ---------------------------------------------------------------- key range
@@ -387,6 +388,32 @@ void attn_bf16_kernel(AttnArgs a) {
     const int per = (t1 - t0 + 3) / 4;
     k0 = min(t1, t0 + kgi * per);
     k1 = min(t1, k0 + per);
+  }
+
+  // ---------------------------------------------------------------- rows
+  // (the query loads are issued first, so that their latency overlaps the
+  // staging loads below and the first tile's loads)
+  bf16x8 qf[RT][ND];
+  int erow[RT];
+  uint64_t ancr[RT];
+  const int row0 = z * RC + rg * RCW;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int row = row0 + rt * 16 + l16;
+    erow[rt] = 0;
+    ancr[rt] = 0;
+#pragma unroll
+    for (int c = 0; c < ND; ++c) qf[rt][c] = bf16x8{};
+    if (row < a.R) {
+      const int t = row / G, hh = row % G;
+      erow[rt] = L - T + t + 1;
+      if constexpr (MODE == kVerify) ancr[rt] = anc_s[t];
+      const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
+                           (((size_t)b * T + t) * a.Hq + g * G + hh) * D + q4 * 8;
+#pragma unroll
+      for (int c = 0; c < ND; ++c)
+        qf[rt][c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + c * 32));
+    }
   }
 
   // ---------------------------------------------------------------- staging
@@ -435,30 +462,6 @@ void attn_bf16_kernel(AttnArgs a) {
     pad_count = red_s[0] + red_s[1] + red_s[2] + red_s[3];
   } else {
     __syncthreads();
-  }
-
-  // ---------------------------------------------------------------- rows
-  bf16x8 qf[RT][ND];
-  int erow[RT];
-  uint64_t ancr[RT];
-  const int row0 = z * RC + rg * RCW;
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int row = row0 + rt * 16 + l16;
-    erow[rt] = 0;
-    ancr[rt] = 0;
-#pragma unroll
-    for (int c = 0; c < ND; ++c) qf[rt][c] = bf16x8{};
-    if (row < a.R) {
-      const int t = row / G, hh = row % G;
-      erow[rt] = L - T + t + 1;
-      if constexpr (MODE == kVerify) ancr[rt] = anc_s[t];
-      const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
-                           (((size_t)b * T + t) * a.Hq + g * G + hh) * D + q4 * 8;
-#pragma unroll
-      for (int c = 0; c < ND; ++c)
-        qf[rt][c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + c * 32));
-    }
   }
 
   // ---------------------------------------------------------------- tile copies
@@ -546,11 +549,14 @@ void attn_bf16_kernel(AttnArgs a) {
     }
   };
 
-  // Nothing but ring copies may be in flight from here on.  The wait is the
-  // compiler's own intrinsic, so it knows the query loads are complete and
-  // inserts no memory-counter wait inside the loop (which, counting the
-  // ring copies too, would drain the prefetch pipeline every tile).
-  __builtin_amdgcn_s_waitcnt(0);
+  // With a shared ring (WK = 1) nothing but ring copies may be in flight
+  // from here on.  The wait is the compiler's own intrinsic, so it knows the
+  // query loads are complete and inserts no memory-counter wait inside the
+  // loop (which, counting the ring copies too, would drain the prefetch
+  // pipeline every tile).  The register-staged path (WK = 4) has only loads
+  // the compiler tracks, so its first tile load is issued without waiting
+  // for the query.
+  if constexpr (WK == 1) __builtin_amdgcn_s_waitcnt(0);
   u32x4 stg[WK == 4 ? Ge::DPT : 1];
   if constexpr (WK == 1) {
 #pragma unroll

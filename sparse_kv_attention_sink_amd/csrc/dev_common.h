@@ -61,11 +61,21 @@ __device__ __forceinline__ void copy16_to_lds(const void* gaddr, uint32_t m0) {
 }
 
 // The same copy from a wave-uniform base (SGPR pair) plus a 32-bit per-lane
-// byte offset: no 64-bit address arithmetic per lane.
+// byte offset: no 64-bit address arithmetic per lane.  The base and m0 go
+// through readfirstlane so that they are scalar whatever the compiler can
+// prove about their uniformity (an "s" operand it believes divergent would
+// otherwise be handed over in VGPRs).
 __device__ __forceinline__ void copy16_to_lds_s(const void* sbase, uint32_t voff, uint32_t m0) {
+  // (readfirstlane returns a signed int: both halves are taken back as
+  // unsigned 32-bit values before they are joined, so the low half is never
+  // sign-extended into the high one)
+  const uint64_t b = reinterpret_cast<uint64_t>(sbase);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint64_t bs = ((uint64_t)hi << 32) | (uint64_t)lo;
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
-               : "v"(voff), "s"(sbase), "s"(m0)
+               : "v"(voff), "s"(reinterpret_cast<const void*>(bs)), "s"(__builtin_amdgcn_readfirstlane(m0))
                : "memory", "m0");
 }
 

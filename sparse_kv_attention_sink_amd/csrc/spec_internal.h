@@ -27,7 +27,7 @@ constexpr int kMaxNodes = 64;                  // one uint64 ancestor mask per n
 constexpr int kTileKeys = 32;                  // keys per KV tile
 constexpr int kMaxGatherKeys = 2048;           // budget indices one workgroup stages in LDS
 constexpr int kMaxPadWords = 1024;             // 32-key pad words one workgroup stages in LDS
-constexpr int kMergeFan = 8;                   // partials one split-merge step reads
+constexpr int kMergeFan = 16;                  // partials one split-merge step reads
 constexpr int kMaxSplits = kMergeFan * kMergeFan;
 
 enum Mode : int { kDraftWindow = 0, kDraftGather = 1, kVerify = 2 };

@@ -111,6 +111,37 @@ def test_verify_never_reads_pads_or_slots_past_the_cache():
                                   oracle.position_ids(case.cache_len, pad, tree.parents))
 
 
+def test_cache_whose_address_has_bit_31_of_its_low_word_set():
+    """Regression: the scalar base of a tile copy is rebuilt from two 32-bit
+    halves; the low half must not be sign-extended.  K and V are placed
+    where the low 32 bits of their addresses are at or above 2^31."""
+    tree = synth.layered_tree(np.random.default_rng(4), (4, 6, 8))       # 18 nodes: shared ring
+    case = small_case(33, T=tree.n)
+    nbytes = case.k.size * 2
+    pool = torch.empty((1 << 31) + 4 * nbytes + 4096, dtype=torch.uint8, device="cuda")
+    base = pool.data_ptr()
+    off = (((1 << 31) - (base & 0xFFFFFFFF)) % (1 << 32) + 255) // 256 * 256
+    assert off + 2 * nbytes <= pool.numel()
+
+    def place(a, at):
+        t = pool[at:at + nbytes].view(torch.bfloat16).view(a.shape)
+        t.copy_(dev(a))
+        assert (t.data_ptr() & 0xFFFFFFFF) >= (1 << 31)
+        return t
+
+    k = place(case.k, off)
+    v = place(case.v, off + nbytes)
+    rng = np.random.default_rng(10)
+    tk = synth.draw_normal(rng, (case.B, case.Hkv, tree.n, case.D), 1.0, "bf16")
+    tv = synth.draw_normal(rng, (case.B, case.Hkv, tree.n, case.D), 1.0, "bf16")
+    out, _, _ = skg.spec_attn_verify_tree(dev(case.q), k, v, dev(case.cache_len), dev(tk), dev(tv),
+                                          dev(tree.parents))
+    ref, _ = oracle.verify_attn_ref(case.q, case.k, case.v, case.cache_len, tk, tv, tree.parents,
+                                    scale=case.scale)
+    assert_close(host64(out), ref, "bf16", "verify, high low-word base")
+    del pool
+
+
 # ------------------------------------------------------------ device range errors
 
 def test_out_of_range_budget_index_poisons_only_its_head():
@@ -229,7 +260,7 @@ def test_workspace_reuse_and_bitwise_determinism():
 
 
 def test_split_count_does_not_change_the_result():
-    """The same sequences in a cache of 4x the capacity get a different split
+    """The same sequences in a cache of 20x the capacity get a different split
     plan (verify splits follow the capacity); both results stay within the
     bar of the oracle and of each other."""
     case = small_case(81, T=3, L=2000, lens=(2000, 1500))
@@ -237,19 +268,19 @@ def test_split_count_does_not_change_the_result():
     rng = np.random.default_rng(12)
     tk = synth.draw_normal(rng, (case.B, case.Hkv, 3, case.D), 1.0, "bf16")
     tv = synth.draw_normal(rng, (case.B, case.Hkv, 3, case.D), 1.0, "bf16")
-    big_k = np.zeros((case.B, case.Hkv, 8000, case.D), dtype=np.uint16)
+    big_k = np.zeros((case.B, case.Hkv, 40000, case.D), dtype=np.uint16)
     big_v = np.zeros_like(big_k)
     big_k[:, :, :2000] = case.k
     big_v[:, :, :2000] = case.v
     dims = skg.make_dims(case.B, case.Hq, case.Hkv, case.D, skg.SPEC_BF16)
-    assert skg.verify_workspace_bytes(dims, 3, 2000) != skg.verify_workspace_bytes(dims, 3, 8000)
+    assert skg.verify_workspace_bytes(dims, 3, 2000) != skg.verify_workspace_bytes(dims, 3, 40000)
     rest = (dev(case.cache_len), dev(tk), dev(tv), dev(par))
     a, _, _ = skg.spec_attn_verify_tree(dev(case.q), dev(case.k), dev(case.v), *rest)
     b, _, _ = skg.spec_attn_verify_tree(dev(case.q), dev(big_k), dev(big_v), *rest)
     ref, _ = oracle.verify_attn_ref(case.q, case.k, case.v, case.cache_len, tk, tv, par,
                                     scale=case.scale)
     assert_close(host64(a), ref, "bf16", "capacity 2000")
-    assert_close(host64(b), ref, "bf16", "capacity 8000")
+    assert_close(host64(b), ref, "bf16", "capacity 40000")
     assert_close(host64(a), host64(b), "bf16", "the two plans")
 
 
