@@ -119,9 +119,13 @@ Plan bf16_plan(const spec_dims* d, int32_t T, int64_t tiles, bool gather, bool v
   p.tps = (int32_t)cdiv(tiles, S);
   p.splits = (int32_t)cdiv(tiles, p.tps);
   p.n_blk = (int32_t)cdiv(p.splits, kMergeFan);
+  // Long register-staged splits take their tiles in chunks (dynamic
+  // balancing across XCDs); budget gathers keep fixed ranges (their indices
+  // are staged per range).
+  if (p.wk == 4 && !gather && p.splits > 1 && tiles >= (int64_t)p.splits * 32) p.dyn = kChunkTiles;
   size_t off = kHeaderBytes;
   p.cnt_off = off;
-  off = align_up(off + (size_t)(groups * (p.n_blk + 1) + 2 * std::max(0, d->batch)) * sizeof(uint32_t), 256);
+  off = align_up(off + (size_t)(groups * (p.n_blk + 2) + 2 * std::max(0, d->batch)) * sizeof(uint32_t), 256);
   if (p.splits > 1) {
     const size_t n = (size_t)groups * p.splits * p.rb;
     p.o_off = off;
@@ -236,6 +240,8 @@ void fill_plan(AttnArgs& a, const Plan& p, void* workspace) {
   a.cnt_l0 = reinterpret_cast<uint32_t*>(ws + p.cnt_off);
   a.cnt_l1 = a.cnt_l0 + groups * p.n_blk;
   a.cnt_pos = a.cnt_l1 + groups;
+  a.cnt_chunk = a.cnt_pos + 2 * (size_t)a.B;
+  a.dyn = p.dyn;
   a.err = reinterpret_cast<uint32_t*>(ws);
 }
 
@@ -430,6 +436,7 @@ spec_status spec_attn_verify_tree(const spec_dims* dims, const void* q, int32_t 
   a.par_sb = parents_stride_b;
   a.pos_ids = pos_ids_or_null;
   fill_plan(a, p, workspace);
+  if (pad_or_null != nullptr) a.dyn = 0;   // pad words are staged per fixed range
   a.out = out;
   a.lse = lse_or_null;
   hipStream_t s = static_cast<hipStream_t>(stream);

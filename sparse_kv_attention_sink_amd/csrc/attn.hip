@@ -562,179 +562,233 @@ void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int u = 0; u < NS - 1; ++u)
       if (k0 + u < k1) issue(k0 + u, u);
-  } else {
-    if (k0 < k1) load_tile_regs<MODE, D>(ks, k0, lane, stg);
+  }
+  // Register-staged splits (WK = 4) of long key ranges: each wave streams a
+  // fixed run of about three quarters of its share, then takes chunks of
+  // a.dyn tiles from a pool shared by the (pair, row block) through an
+  // arrival-style counter, so that waves on faster XCDs take over work of
+  // slower ones.  A wave requests its next chunk right after issuing the
+  // loads of its current run's last tile: memory operations complete in
+  // order, so a request issued earlier would hold up every later tile wait.
+  const bool dyn = WK == 4 && MODE != kDraftGather && a.dyn > 0;
+  uint32_t* const c_cnt = a.cnt_chunk + (size_t)pair * a.n_rb + z;
+  const int C = dyn ? a.dyn : 1;
+  const int n_chunks = (total + C - 1) / C;
+  const int wpp = a.splits * 4;                       // waves per (pair, row block)
+  const int F = dyn ? (n_chunks * 3 / 4) / wpp : 0;   // fixed chunks per wave
+  const int pool0 = wpp * F;                          // first pooled chunk
+  int t_first = k0 < k1 ? k0 : -1, run_end = k1, c_next = 0;
+  bool pending = false;   // a pool request is on its way
+  auto request = [&]() __attribute__((always_inline)) {
+    if (lane == 0) c_next = (int)__hip_atomic_fetch_add(c_cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    pending = true;
+  };
+  // first tile of the requested pool chunk, or -1
+  auto take = [&]() __attribute__((always_inline)) -> int {
+    const int c = pool0 + __builtin_amdgcn_readfirstlane(c_next);
+    pending = false;
+    if (c >= n_chunks) return -1;
+    run_end = min((c + 1) * C, total);
+    return c * C;
+  };
+  if (dyn) {
+    const int wi = s * 4 + kgi;
+    const int a0 = min(wi * F * C, total), a1 = min((wi + 1) * F * C, total);
+    if (a0 < a1) {
+      t_first = a0;
+      run_end = a1;
+    } else if (pool0 < n_chunks) {
+      request();
+      t_first = take();
+    } else {
+      t_first = -1;
+    }
   }
 
-  // Unrolled by the ring depth, so that a tile's stage is a constant.
-  for (int tb = k0; tb < k1; tb += NS) {
-#pragma unroll
-    for (int st = 0; st < NS; ++st) {
-      const int t = tb + st;
-      if (t >= k1) break;
-      uint32_t so;   // stage offset
-      if constexpr (WK == 1) {
-        wait_tiles<DPW, NS - 2>(k1 - 1 - t);
-        barrier_only();   // every wave's copies of tile t landed; tile t-1 is consumed
-        if (t + NS - 1 < k1) issue(t + NS - 1, (st + NS - 1) % NS);
-        so = st * SB;
-      } else {
-        // the wave's own stage: LDS operations of a wave execute in order, so
-        // these writes land after the previous tile's reads and before this
-        // tile's; the next tile's loads are in flight while this one is used
-        so = 0;
-        store_tile_lds<D>(ring_base, lane, stg);
-        if (t + 1 < k1) load_tile_regs<MODE, D>(ks, t + 1, lane, stg);
-      }
-      const bool tree_tile = MODE == kVerify && t >= cache_tiles;
-      // This tile's pad word (verify), read before the fragment reads so that
-      // waiting for it never waits for them; it is uniform, so the visibility
-      // test below is a scalar branch.
-      uint32_t pw = 0u;
-      if constexpr (MODE == kVerify) {
-        if (!tree_tile && a.pad != nullptr) pw = __builtin_amdgcn_readfirstlane(padbits_s[t - t0]);
-      }
-      const bool full = !tree_tile && (t + 1) * kTileKeys <= n_view && !row_masks && pw == 0u;
+  // One tile: scores, masks, online softmax and P.V for keys of tile t,
+  // whose K and V rows sit at stage offset `so` of this wave's ring.
+  const uint8_t* const pad_ptr = a.pad;
+  const int n_sink_ = a.n_sink, window_ = a.window;
+  auto tile_body = [&](const int t, const uint32_t so) __attribute__((always_inline)) {
+    const bool tree_tile = MODE == kVerify && t >= cache_tiles;
+    // This tile's pad word (verify), read before the fragment reads so that
+    // waiting for it never waits for them; it is uniform, so the visibility
+    // test below is a scalar branch.
+    uint32_t pw = 0u;
+    if constexpr (MODE == kVerify) {
+      if (!tree_tile && pad_ptr != nullptr) pw = __builtin_amdgcn_readfirstlane(padbits_s[t - t0]);
+    }
+    const bool full = !tree_tile && (t + 1) * kTileKeys <= n_view && !row_masks && pw == 0u;
 
-      // K fragments (A operand of S^T): key h*16 + l16, head-dim chunk cc*4 + q4;
-      // V^T fragments (A operand of O^T) for every d tile, read now so that
-      // their latency hides behind the scores and the softmax.
-      bf16x8 kf[2][ND], vf[NDT];
+    // K fragments (A operand of S^T): key h*16 + l16, head-dim chunk cc*4 + q4;
+    // V^T fragments (A operand of O^T) for every d tile, read now so that
+    // their latency hides behind the scores and the softmax.
+    bf16x8 kf[2][ND], vf[NDT];
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int cc = 0; cc < ND; ++cc) kf[h][cc] = lds_load_b128(koff[cc] + so + h * 16 * ROWB);
+      for (int cc = 0; cc < ND; ++cc) kf[h][cc] = lds_load_b128(koff[cc] + so + h * 16 * ROWB);
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const s16x4 v0 = lds_read_tr16(voff[dt] + so);
-        const s16x4 v1 = lds_read_tr16(voff[dt] + so + 16 * ROWB);
-        vf[dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+    for (int dt = 0; dt < NDT; ++dt) {
+      const s16x4 v0 = lds_read_tr16(voff[dt] + so);
+      const s16x4 v1 = lds_read_tr16(voff[dt] + so + 16 * ROWB);
+      vf[dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+    f32x4 sc[RT][2];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int cc = 0; cc < ND; ++cc)
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[h][cc], qf[rt][cc], c, 0, 0, 0);
+        sc[rt][h] = c;
       }
-      f32x4 sc[RT][2];
+
+    // Visibility of this lane's 8 keys, local index e = h*4 + i, tile key
+    // h*16 + q4*4 + i.  `full` tiles (every key visible to every row) skip it.
+    uint32_t kmask = 0xffu;
+    if constexpr (MODE == kVerify) {
+      if (!tree_tile && !full) {
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int cc = 0; cc < ND; ++cc)
-            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[h][cc], qf[rt][cc], c, 0, 0, 0);
-          sc[rt][h] = c;
+        for (int e = 0; e < 8; ++e) {
+          const int kk = (e >> 2) * 16 + q4 * 4 + (e & 3);
+          if (t * kTileKeys + kk >= n_view || ((pw >> kk) & 1u)) kmask &= ~(1u << e);
         }
+      }
+    } else if (!full) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int kk = (e >> 2) * 16 + q4 * 4 + (e & 3);
+        if (t * kTileKeys + kk >= n_view) kmask &= ~(1u << e);
+      }
+    }
+    int jpos[8];
+    if (row_masks) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int kk = (e >> 2) * 16 + q4 * 4 + (e & 3);
+        jpos[e] = view_pos<MODE>(ks, min(t * kTileKeys + kk, n_view - 1));
+      }
+    }
 
-      // Visibility of this lane's 8 keys, local index e = h*4 + i, tile key
-      // h*16 + q4*4 + i.  `full` tiles (every key visible to every row) skip it.
-      uint32_t kmask = 0xffu;
-      if constexpr (MODE == kVerify) {
-        if (!tree_tile && !full) {
+    // Scores of this lane's row, masked (-inf).
+    float x[RT][8];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[rt][e] = sc[rt][e >> 2][e & 3];
+      if (!full) {
+        uint32_t rm = kmask;
+        if (tree_tile) {
+          const uint32_t aw = (uint32_t)(ancr[rt] >> ((t - cache_tiles) * kTileKeys));
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int kk = (e >> 2) * 16 + q4 * 4 + (e & 3);
-            if (t * kTileKeys + kk >= n_view || ((pw >> kk) & 1u)) kmask &= ~(1u << e);
+            if (!((aw >> kk) & 1u)) rm &= ~(1u << e);
+          }
+        } else if (row_masks) {
+          const int er = erow[rt];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            bool vis = jpos[e] < er;
+            if (MODE == kDraftWindow) vis = vis && (jpos[e] < n_sink_ || jpos[e] >= er - window_);
+            if (!vis) rm &= ~(1u << e);
           }
         }
-      } else if (!full) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int kk = (e >> 2) * 16 + q4 * 4 + (e & 3);
-          if (t * kTileKeys + kk >= n_view) kmask &= ~(1u << e);
-        }
+        for (int e = 0; e < 8; ++e) x[rt][e] = ((rm >> e) & 1u) ? x[rt][e] : -INFINITY;
       }
-      int jpos[8];
-      if (row_masks) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int kk = (e >> 2) * 16 + q4 * 4 + (e & 3);
-          jpos[e] = view_pos<MODE>(ks, min(t * kTileKeys + kk, n_view - 1));
-        }
-      }
+    }
 
-      // Scores of this lane's row, masked (-inf).
-      float x[RT][8];
+    // p = 2^(score*c2 - m) against the running maximum m.  Lazy rescale:
+    // m is raised only when some p of the wave exceeds 2^8 (a lane's sum
+    // of p above 2^8 is the test: it holds whenever one p does), so every
+    // p used is at most 2^8, safe in fp32 and bf16; the final o = acc / l
+    // is the same either way.  The branch is wave-uniform and rare (at the
+    // first visible key of a row and when scores climb by more than 8 in
+    // log2 units), so the accumulators stay in the MFMA registers.
+    float p[RT][8], ps[RT];
+    bool grow = false;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      ps[rt] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[rt][e] = __builtin_amdgcn_exp2f(fmaf(x[rt][e], c2, -m[rt]));
+        ps[rt] += p[rt][e];
+      }
+      grow = grow || ps[rt] > 256.f;
+    }
+    if (__builtin_expect(__any(grow), 0)) {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
+        float mx = x[rt][0];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[rt][e] = sc[rt][e >> 2][e & 3];
-        if (!full) {
-          uint32_t rm = kmask;
-          if (tree_tile) {
-            const uint32_t aw = (uint32_t)(ancr[rt] >> ((t - cache_tiles) * kTileKeys));
+        for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[rt][e]);
+        mx = fmaxf(mx, shfl_xor(mx, 16));
+        mx = fmaxf(mx, shfl_xor(mx, 32));
+        const float mn = fmaxf(m[rt], mx * c2);
+        const float alpha = __builtin_amdgcn_exp2f(m[rt] - mn);
+        m[rt] = mn;
+        lsum[rt] *= alpha;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int kk = (e >> 2) * 16 + q4 * 4 + (e & 3);
-              if (!((aw >> kk) & 1u)) rm &= ~(1u << e);
-            }
-          } else if (row_masks) {
-            const int er = erow[rt];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              bool vis = jpos[e] < er;
-              if (MODE == kDraftWindow) vis = vis && (jpos[e] < a.n_sink || jpos[e] >= er - a.window);
-              if (!vis) rm &= ~(1u << e);
-            }
-          }
-#pragma unroll
-          for (int e = 0; e < 8; ++e) x[rt][e] = ((rm >> e) & 1u) ? x[rt][e] : -INFINITY;
-        }
-      }
-
-      // p = 2^(score*c2 - m) against the running maximum m.  Lazy rescale:
-      // m is raised only when some p of the wave exceeds 2^8 (a lane's sum
-      // of p above 2^8 is the test: it holds whenever one p does), so every
-      // p used is at most 2^8, safe in fp32 and bf16; the final o = acc / l
-      // is the same either way.  The branch is wave-uniform and rare (at the
-      // first visible key of a row and when scores climb by more than 8 in
-      // log2 units), so the accumulators stay in the MFMA registers.
-      float p[RT][8], ps[RT];
-      bool grow = false;
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
+        for (int dt = 0; dt < NDT; ++dt) acc[rt][dt] *= alpha;
         ps[rt] = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          p[rt][e] = __builtin_amdgcn_exp2f(fmaf(x[rt][e], c2, -m[rt]));
+          p[rt][e] = __builtin_amdgcn_exp2f(fmaf(x[rt][e], c2, -mn));
           ps[rt] += p[rt][e];
         }
-        grow = grow || ps[rt] > 256.f;
       }
-      if (__builtin_expect(__any(grow), 0)) {
+    }
+    uint32_t pf[RT][4];
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          float mx = x[rt][0];
+    for (int rt = 0; rt < RT; ++rt) {
+      lsum[rt] += ps[rt];
 #pragma unroll
-          for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[rt][e]);
-          mx = fmaxf(mx, shfl_xor(mx, 16));
-          mx = fmaxf(mx, shfl_xor(mx, 32));
-          const float mn = fmaxf(m[rt], mx * c2);
-          const float alpha = __builtin_amdgcn_exp2f(m[rt] - mn);
-          m[rt] = mn;
-          lsum[rt] *= alpha;
+      for (int w = 0; w < 4; ++w) pf[rt][w] = pack_bf16x2(p[rt][2 * w], p[rt][2 * w + 1]);
+    }
+
+    // O^T += V^T . P^T
 #pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) acc[rt][dt] *= alpha;
-          ps[rt] = 0.f;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            p[rt][e] = __builtin_amdgcn_exp2f(fmaf(x[rt][e], c2, -mn));
-            ps[rt] += p[rt][e];
-          }
-        }
-      }
-      uint32_t pf[RT][4];
+    for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        lsum[rt] += ps[rt];
-#pragma unroll
-        for (int w = 0; w < 4; ++w) pf[rt][w] = pack_bf16x2(p[rt][2 * w], p[rt][2 * w + 1]);
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(pf[rt][0], pf[rt][1], pf[rt][2], pf[rt][3]));
+        acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pb, acc[rt][dt], 0, 0, 0);
       }
+  };
 
-      // O^T += V^T . P^T
+  if constexpr (WK == 1) {
+    // Unrolled by the ring depth, so that a tile's stage is a constant.
+    for (int tb = k0; tb < k1; tb += NS) {
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(pf[rt][0], pf[rt][1], pf[rt][2], pf[rt][3]));
-          acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pb, acc[rt][dt], 0, 0, 0);
-        }
+      for (int st = 0; st < NS; ++st) {
+        const int t = tb + st;
+        if (t >= k1) break;
+        wait_tiles<DPW, NS - 2>(k1 - 1 - t);
+        barrier_only();   // every wave's copies of tile t landed; tile t-1 is consumed
+        if (t + NS - 1 < k1) issue(t + NS - 1, (st + NS - 1) % NS);
+        tile_body(t, st * SB);
+      }
+    }
+  } else {
+    // The wave's own stage: LDS operations of a wave execute in order, so
+    // the stores of tile t land after the reads of tile t-1 and before its
+    // own; the next tile's loads are in flight while tile t is used.
+    int t = t_first;
+    if (t >= 0) load_tile_regs<MODE, D>(ks, t, lane, stg);
+    if (dyn && t >= 0 && t == run_end - 1 && pool0 < n_chunks) request();
+    while (t >= 0) {
+      store_tile_lds<D>(ring_base, lane, stg);
+      int tn = t + 1;
+      if (tn >= run_end) tn = pending ? take() : -1;
+      if (tn >= 0) load_tile_regs<MODE, D>(ks, tn, lane, stg);
+      if (dyn && tn >= 0 && tn == run_end - 1 && pool0 < n_chunks) request();
+      tile_body(t, 0u);
+      t = tn;
     }
   }
 
@@ -885,7 +939,13 @@ void attn_bf16_kernel(AttnArgs a) {
     if (d0 == 0 && lse_out != nullptr) lse_out[oi] = lse2 * kLn2;
   };
   if (!arrive_last(a.cnt_l0 + grp * nb + blk, bsz)) return;
+  // The (pair, row block)'s final merger: every split has arrived, so no
+  // wave grabs chunks any more and the chunk counter can start over.
+  auto reset_chunks = [&]() __attribute__((always_inline)) {
+    if (a.dyn > 0 && tid == 0) __hip_atomic_store(c_cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
   if (nb == 1) {
+    reset_chunks();
     merge_partials<D, RC>(o_rs, l_rs, 0, S, rows, final_sink);
     return;
   }
@@ -897,6 +957,7 @@ void attn_bf16_kernel(AttnArgs a) {
                           if (d0 == 0) store_sc1_f1(l1_rs, (uint32_t)((blk * RC + rl) * 4), lse2);
                         });
   if (!arrive_last(a.cnt_l1 + grp, nb)) return;
+  reset_chunks();
   merge_partials<D, RC>(o1_rs, l1_rs, 0, nb, rows, final_sink);
 }
 

@@ -29,6 +29,7 @@ constexpr int kMaxGatherKeys = 2048;           // budget indices one workgroup s
 constexpr int kMaxPadWords = 1024;             // 32-key pad words one workgroup stages in LDS
 constexpr int kMergeFan = 16;                  // partials one split-merge step reads
 constexpr int kMaxSplits = kMergeFan * kMergeFan;
+constexpr int kChunkTiles = 8;                 // tiles per dynamically taken chunk
 
 enum Mode : int { kDraftWindow = 0, kDraftGather = 1, kVerify = 2 };
 
@@ -74,6 +75,8 @@ struct AttnArgs {
   uint32_t* cnt_l0;       // [pair][n_rb][n_blk] arrival counters (zero between calls)
   uint32_t* cnt_l1;       // [pair][n_rb]
   uint32_t* cnt_pos;      // [B][2] pad-count arrival (verify positions)
+  uint32_t* cnt_chunk;    // bf16 path: [pair][n_rb] next tile chunk (dynamic splits)
+  int32_t dyn;            // bf16 path: tiles per dynamically taken chunk, 0 = fixed ranges
   void* out;              // final output
   float* lse;             // final lse (natural log) or null
   uint32_t* err;          // device error word
@@ -85,6 +88,7 @@ struct Plan {
   size_t cnt_off = 0, o_off = 0, lse_off = 0, o1_off = 0, lse1_off = 0, anc_off = 0, bad_off = 0,
          total = 0;
   int32_t n_blk = 1;
+  int32_t dyn = 0;          // tiles per dynamically taken chunk (0: fixed split ranges)
 };
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
