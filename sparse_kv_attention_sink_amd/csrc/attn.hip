@@ -223,58 +223,76 @@ __device__ __forceinline__ void store_tile_lds(uint32_t stage, int lane, const u
 // o (normalised by its own softmax sum) at o_rs[((p0 + p) * RC + rl) * D + d]
 // and its log2 sum-exp at l_rs[(p0 + p) * RC + rl].  For every (row, 4 head-
 // dim values) item of the first `rows` rows, all loads are issued before any
-// is used (partials past n re-read the last one and get weight 0), and
+// is used, two items at a time (partials past n re-read the last one and get
+// weight 0), and
 // sink(rl, d0, o[4], lse2) receives sum_p 2^(x_p - M) o_p / sum_p 2^(x_p - M)
 // and M + log2 sum_p 2^(x_p - M), M = max_p x_p: NaN if any partial is NaN,
 // o = 0 and lse = -inf if every partial is empty.
 template <int D, int RC, typename Sink>
 __device__ __forceinline__ void merge_partials(__amdgpu_buffer_rsrc_t o_rs, __amdgpu_buffer_rsrc_t l_rs,
                                                int p0, int n, int rows, Sink sink) {
-  for (int it = threadIdx.x; it < RC * (D / 4); it += 256) {
-    const int rl = it / (D / 4), d0 = (it % (D / 4)) * 4;
-    if (rl >= rows) continue;
-    float x[kMergeFan];
-    f32x4 ov[kMergeFan];
+  constexpr int kItems = RC * (D / 4);
+  constexpr int kPerThread = (kItems + 255) / 256;
+  // items whose loads are in flight together (one for D = 64, where the
+  // registers of a second item would cost the main loop occupancy)
+  constexpr int U = (kPerThread >= 2 && D == 128) ? 2 : 1;
+  for (int i0 = 0; i0 < kPerThread; i0 += U) {
+    float x[U][kMergeFan];
+    f32x4 ov[U][kMergeFan];
 #pragma unroll
-    for (int p = 0; p < kMergeFan; ++p) {
-      const int pp = p0 + min(p, n - 1);
-      x[p] = load_sc1_f1(l_rs, (uint32_t)((pp * RC + rl) * 4));
-      ov[p] = load_sc1_f4(o_rs, (uint32_t)(((pp * RC + rl) * D + d0) * 4));
-    }
-    float M = -INFINITY;
-    bool nan = false;
-#pragma unroll
-    for (int p = 0; p < kMergeFan; ++p)
-      if (p < n) {
-        nan |= isnan(x[p]);
-        M = fmaxf(M, x[p]);
-      }
-    float W = 0.f, o[4] = {0.f, 0.f, 0.f, 0.f};
-    if (!nan && M != -INFINITY) {
+    for (int u = 0; u < U; ++u) {
+      const int it = (int)threadIdx.x + (i0 + u) * 256;
+      const int rl = it / (D / 4), d0 = (it % (D / 4)) * 4;
+      const bool live = it < kItems && rl < rows;
 #pragma unroll
       for (int p = 0; p < kMergeFan; ++p) {
-        const float f = p < n ? __builtin_amdgcn_exp2f(x[p] - M) : 0.f;
-        W += f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] += f * ov[p][e];
+        const int pp = p0 + min(p, n - 1);
+        // a dead item reads row 0 of the first partial (always in range)
+        const int r = live ? rl : 0, dd = live ? d0 : 0;
+        x[u][p] = load_sc1_f1(l_rs, (uint32_t)((pp * RC + r) * 4));
+        ov[u][p] = load_sc1_f4(o_rs, (uint32_t)(((pp * RC + r) * D + dd) * 4));
       }
     }
-    float lse2;
-    if (nan) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = NAN;
-      lse2 = NAN;
-    } else if (M == -INFINITY || !(W > 0.f)) {
+    for (int u = 0; u < U; ++u) {
+      const int it = (int)threadIdx.x + (i0 + u) * 256;
+      const int rl = it / (D / 4), d0 = (it % (D / 4)) * 4;
+      if (it >= kItems || rl >= rows) continue;
+      float M = -INFINITY;
+      bool nan = false;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = 0.f;
-      lse2 = -INFINITY;
-    } else {
-      const float inv = 1.f / W;
+      for (int p = 0; p < kMergeFan; ++p)
+        if (p < n) {
+          nan |= isnan(x[u][p]);
+          M = fmaxf(M, x[u][p]);
+        }
+      float W = 0.f, o[4] = {0.f, 0.f, 0.f, 0.f};
+      if (!nan && M != -INFINITY) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] *= inv;
-      lse2 = M + log2f(W);
+        for (int p = 0; p < kMergeFan; ++p) {
+          const float f = p < n ? __builtin_amdgcn_exp2f(x[u][p] - M) : 0.f;
+          W += f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] += f * ov[u][p][e];
+        }
+      }
+      float lse2;
+      if (nan) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = NAN;
+        lse2 = NAN;
+      } else if (M == -INFINITY || !(W > 0.f)) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = 0.f;
+        lse2 = -INFINITY;
+      } else {
+        const float inv = 1.f / W;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] *= inv;
+        lse2 = M + log2f(W);
+      }
+      sink(rl, d0, o, lse2);
     }
-    sink(rl, d0, o, lse2);
   }
 }
 
