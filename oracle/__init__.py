@@ -21,7 +21,9 @@ Sources (page title, then the passage):
   nodes; batched verification pads accepted tokens, remaps position IDs to
   ignore padding and gives cached padding slots -inf.
 * "SpecPV: Improving Self-Speculative Decoding for Long-Context Generation via
-  Partial Verification" -- section 4.1 "Metrics": the accept length may be 0.
+  Partial Verification" -- section 4.1 "Metrics": the accept length may be 0;
+  section 3.3: candidates that were not accepted leave the cache once
+  verification is done.
 
 Pin status: every public function here is pinned by ``tests/test_oracle_*.py``
 against something other than itself (library SDPA, closed forms, brute force,
@@ -32,7 +34,8 @@ from .bf16 import decode_bf16, as_f64
 from .attention import (draft_view, draft_attn_ref, tree_depths, tree_ancestors,
                         position_ids, verify_keys, verify_attn_ref)
 from .accept import argmax_ref, accept_ref, accept_bruteforce
+from .commit import commit_ref
 
 __all__ = ["decode_bf16", "as_f64", "draft_view", "draft_attn_ref", "tree_depths",
            "tree_ancestors", "position_ids", "verify_keys", "verify_attn_ref",
-           "argmax_ref", "accept_ref", "accept_bruteforce"]
+           "argmax_ref", "accept_ref", "accept_bruteforce", "commit_ref"]
