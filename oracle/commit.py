@@ -19,9 +19,10 @@ Reading of what the pages leave open:
 * Every sequence of the batch appends the same P = 1 + max_b tau_b slots;
   slots past a sequence's bonus slot are padding (pad byte 1), and
   cache_len grows by P.
-* A sequence whose accept length lies outside [0, max_depth], or whose path
-  names a node outside [0, N), contributes tau = 0 to P and appends P
-  padding slots (nothing of it is committed); the error is reported.
+* A sequence whose accept length lies outside [0, min(max_depth, N)] (a root
+  path has at most N nodes), or whose path names a node outside [0, N),
+  contributes tau = 0 to P and appends P padding slots (nothing of it is
+  committed); the error is reported.
 * A sequence whose cache_len lies outside [0, capacity - P] is left as it
   is (no slot written, cache_len unchanged); the error is reported.
 """
@@ -34,7 +35,7 @@ ERR_COMMIT = 16
 
 
 def _valid(tau: int, path_b, n_nodes: int, max_depth: int) -> bool:
-    if tau < 0 or tau > max_depth:
+    if tau < 0 or tau > min(max_depth, n_nodes):
         return False
     return all(0 <= int(path_b[j]) < n_nodes for j in range(tau))
 

@@ -188,6 +188,16 @@ def test_bad_accept_results_append_padding_only():
     assert k2[2, 0, 4:6].all() and not k2[2, 0, 6].any()
 
 
+def test_accept_length_beyond_the_node_count_is_invalid():
+    z = np.zeros((1, 1, 16, 2), dtype=np.float32)
+    tk = np.ones((1, 1, 2, 2), dtype=np.float32)
+    _, _, cl2, pad2, P, err = oracle.commit_ref(z, z, [4], np.zeros((1, 16), np.uint8), tk, tk,
+                                                [3], [[0, 1, 1]], 5)
+    assert err == oracle.commit.ERR_COMMIT and P == 1
+    np.testing.assert_array_equal(cl2, [5])
+    assert pad2[0, 4] == 1
+
+
 def test_cache_overflow_leaves_the_sequence_alone():
     z = np.zeros((2, 1, 8, 2), dtype=np.float32)
     tk = np.ones((2, 1, 3, 2), dtype=np.float32)
