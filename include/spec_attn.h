@@ -2,7 +2,7 @@
  * spec_attn.h -- C ABI of libspecattn, the attention hot path of long-context
  * speculative decoding on AMD Instinct MI355X (gfx950).
  *
- * Three operations, each a set of HIP kernels launched asynchronously on the
+ * Four operations, each a set of HIP kernels launched asynchronously on the
  * caller's stream:
  *
  *   spec_attn_draft_sparse  draft-phase attention over a sparse view of the KV
@@ -13,6 +13,8 @@
  *                           padded ragged batches and remapped positions.
  *   spec_accept_greedy      greedy tree acceptance: an argmax per node, then
  *                           the longest accepted root path and the bonus token.
+ *   spec_kv_commit          append the accepted path's K/V to the cache,
+ *                           padding the batch to one uniform length.
  *
  * Conventions for every call
  *   - Tensor arguments are DEVICE pointers owned by the caller.  The library
@@ -51,7 +53,8 @@
  *   [SM] "SpecMemo: Speculative Decoding is in Your Pocket" (Pith review),
  *        "What carries the argument" and Figure 9.
  *   [PV] "SpecPV: Improving Self-Speculative Decoding for Long-Context
- *        Generation via Partial Verification", section 4.1 "Metrics".
+ *        Generation via Partial Verification", section 4.1 "Metrics" and
+ *        section 3.3 "Rectified with Full Verification".
  */
 #ifndef SPEC_ATTN_H
 #define SPEC_ATTN_H
@@ -80,10 +83,13 @@ enum { SPEC_F32 = 0, SPEC_BF16 = 1 };
 
 /* Bits of the device error word (spec_device_status). */
 enum {
-  SPEC_DEV_CACHE_LEN = 1u,   /* cache_len[b] < 0, > capacity, or < n_q_tokens (draft) */
+  SPEC_DEV_CACHE_LEN = 1u,   /* cache_len[b] < 0, > capacity, < n_q_tokens (draft), or
+                                > capacity - P (kv commit) */
   SPEC_DEV_INDEX = 2u,       /* a budget index outside [0, cache_len[b]) */
   SPEC_DEV_PARENT = 4u,      /* parents[i] not in [-1, i) */
-  SPEC_DEV_DEPTH = 8u        /* accepted path longer than max_depth */
+  SPEC_DEV_DEPTH = 8u,       /* accepted path longer than max_depth */
+  SPEC_DEV_COMMIT = 16u      /* kv commit: accept length outside [0, min(max_depth, N)]
+                                or a path entry outside [0, N) */
 };
 
 typedef struct {
@@ -108,6 +114,16 @@ typedef struct {
   int64_t stride_t;       /* >= D */
   int32_t capacity;       /* allocated slots per (b, h); cache_len[b] <= capacity */
 } spec_kv;
+
+/* The same layout for a K/V pair the library writes (spec_kv_commit). */
+typedef struct {
+  void* k;
+  void* v;
+  int64_t stride_b;
+  int64_t stride_h;
+  int64_t stride_t;
+  int32_t capacity;
+} spec_kv_mut;
 
 /*
  * Draft attention over a sparse view of the cache ([WM] "What carries the
@@ -191,6 +207,48 @@ spec_status spec_accept_greedy(int32_t batch, int32_t n_nodes, int32_t vocab,
                                int32_t* accept_len, int32_t* accept_path, int32_t* bonus,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * KV commit of the accepted path ([SM] "What carries the argument", Figure 9;
+ * [PV] section 3.3), the step after spec_accept_greedy.
+ *
+ * For every sequence b with a valid acceptance result (0 <= accept_len[b]
+ * <= min(max_depth, N) and accept_path[b][j] in [0, N) for j < accept_len[b]),
+ * the K and V rows of the accepted nodes accept_path[b][0..tau) are copied,
+ * in path order, from `tree` ([B][Hkv][N][D]) into the cache slots
+ * [cache_len[b], cache_len[b] + tau).  Slot cache_len[b] + tau is the bonus
+ * token's: it is marked valid and no K/V is written there (the caller's next
+ * forward pass computes it; that token is the next anchor).  The whole batch
+ * appends the same P = 1 + max_b tau_b slots (invalid sequences count 0):
+ * pad[b][cache_len[b] + j] = 0 for j <= tau, 1 for tau < j < P, and
+ * cache_len[b] grows by P.  *n_appended_or_null receives P.
+ *
+ * A sequence with an invalid acceptance result raises SPEC_DEV_COMMIT,
+ * commits nothing and appends P padding slots.  A sequence whose
+ * cache_len[b] is outside [0, capacity - P] raises SPEC_DEV_CACHE_LEN and is
+ * left untouched (no slot written, cache_len unchanged).
+ *
+ * The tree rows of a (sequence, KV head) may alias that pair's cache slots at
+ * or after cache_len[b] (node n at slot cache_len[b] + n + c, c >= 0, as when
+ * verify wrote the tree K/V into the cache): the copy never overwrites a row
+ * it has still to read.  Apart from that, the cache, the tree, pad and the
+ * integer arrays must not overlap.
+ *
+ * dtype SPEC_F32 or SPEC_BF16 (element size only: the commit copies bytes);
+ * head_dim 64 or 128; cache and tree follow the spec_kv layout rules.
+ * cache_len int32 [B] (read and written), pad uint8 [B][pad_stride_b] with
+ * pad_stride_b >= capacity, accept_len int32 [B], accept_path int32
+ * [B][max_depth] (as written by spec_accept_greedy), 1 <= N <= 64,
+ * max_depth >= 1.  batch = 0 launches nothing (pointers may be NULL).
+ * Workspace: spec_commit_workspace_bytes() bytes (the device error word).
+ */
+spec_status spec_kv_commit(int32_t batch, int32_t n_kv_heads, int32_t head_dim, int32_t dtype,
+                           const spec_kv_mut* cache, int32_t* cache_len,
+                           uint8_t* pad, int64_t pad_stride_b,
+                           const spec_kv* tree, int32_t n_nodes,
+                           const int32_t* accept_len, const int32_t* accept_path,
+                           int32_t max_depth, int32_t* n_appended_or_null,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace sizes in bytes (0 on invalid arguments; see spec_last_error).
  * max_view_len for the draft: min(capacity, n_sink + window + n_q_tokens - 1)
  * in window mode, the budget in budget mode (a larger value is always safe).
@@ -200,6 +258,7 @@ size_t spec_draft_workspace_bytes(const spec_dims* dims, int32_t n_q_tokens,
 size_t spec_verify_workspace_bytes(const spec_dims* dims, int32_t n_nodes,
                                    int32_t capacity);
 size_t spec_accept_workspace_bytes(int32_t batch, int32_t n_nodes, int32_t vocab);
+size_t spec_commit_workspace_bytes(void);
 
 /* Waits for `stream`, reads and clears the device error word of `workspace`.
  * Returns SPEC_OK, SPEC_E_DEVICE_RANGE (bits in *bits_or_null) or

@@ -29,10 +29,12 @@ SPEC_DEV_CACHE_LEN = 1
 SPEC_DEV_INDEX = 2
 SPEC_DEV_PARENT = 4
 SPEC_DEV_DEPTH = 8
+SPEC_DEV_COMMIT = 16
 
 EXPORTED = [
-    "spec_attn_draft_sparse", "spec_attn_verify_tree", "spec_accept_greedy",
+    "spec_attn_draft_sparse", "spec_attn_verify_tree", "spec_accept_greedy", "spec_kv_commit",
     "spec_draft_workspace_bytes", "spec_verify_workspace_bytes", "spec_accept_workspace_bytes",
+    "spec_commit_workspace_bytes",
     "spec_device_status", "spec_status_string", "spec_last_error", "spec_abi_version",
 ]
 
@@ -74,6 +76,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.spec_attn_verify_tree.restype = I32
     lib.spec_accept_greedy.argtypes = [I32, I32, I32, P, P, P, I64, I32, P, P, P, P, SZ, P]
     lib.spec_accept_greedy.restype = I32
+    lib.spec_kv_commit.argtypes = [I32, I32, I32, I32, P, P, P, I64, P, I32, P, P, I32, P, P, SZ, P]
+    lib.spec_kv_commit.restype = I32
+    lib.spec_commit_workspace_bytes.argtypes = []
+    lib.spec_commit_workspace_bytes.restype = SZ
     lib.spec_draft_workspace_bytes.argtypes = [P, I32, I32]
     lib.spec_draft_workspace_bytes.restype = SZ
     lib.spec_verify_workspace_bytes.argtypes = [P, I32, I32]
@@ -270,6 +276,46 @@ def spec_accept_greedy(logits, draft_tokens, parents, max_depth, *, accept_len=N
                                 _ptr(workspace), workspace.numel(), _stream(logits))
     _check(st)
     return accept_len, accept_path, bonus
+
+
+def commit_workspace_bytes() -> int:
+    return int(load().spec_commit_workspace_bytes())
+
+
+def spec_kv_commit(k_cache, v_cache, cache_len, pad, tree_k, tree_v, accept_len, accept_path, *,
+                   n_appended=None, workspace=None):
+    """Append each sequence's accepted path (the K/V rows of
+    ``accept_path[b, :accept_len[b]]`` in ``tree_k``/``tree_v``) to its cache
+    after ``cache_len[b]``, pad the batch to one uniform length P, and advance
+    ``cache_len`` and ``pad`` in place.  Returns ``n_appended`` (int32 [1] = P)."""
+    lib = load()
+    _on_gpu(k_cache, v_cache, cache_len, pad, tree_k, tree_v, accept_len, accept_path)
+    B, Hkv, _, D = k_cache.shape
+    if tree_k.shape[0] != B or tree_k.shape[1] != Hkv or tree_k.shape[3] != D or \
+            tree_k.dtype != k_cache.dtype:
+        raise ValueError("tree K/V must be [B, Hkv, N, D] of the cache's dtype")
+    if cache_len.dtype != torch.int32 or cache_len.numel() != B or not cache_len.is_contiguous():
+        raise ValueError("cache_len must be a contiguous int32 [B] tensor")
+    if pad.dtype != torch.uint8 or pad.dim() != 2 or pad.shape[0] != B or pad.stride(1) != 1 or \
+            pad.shape[1] < k_cache.shape[2]:
+        raise ValueError("pad must be uint8 [B, >= L_cap]")
+    if accept_len.dtype != torch.int32 or accept_len.numel() != B or not accept_len.is_contiguous():
+        raise ValueError("accept_len must be a contiguous int32 [B] tensor")
+    if accept_path.dtype != torch.int32 or accept_path.dim() != 2 or accept_path.shape[0] != B or \
+            not accept_path.is_contiguous():
+        raise ValueError("accept_path must be a contiguous int32 [B, max_depth] tensor")
+    kv = _kv(k_cache, v_cache)
+    tkv = _kv(tree_k, tree_v)
+    if n_appended is None:
+        n_appended = torch.empty(1, dtype=torch.int32, device=k_cache.device)
+    if workspace is None:
+        workspace = new_workspace(commit_workspace_bytes(), k_cache.device)
+    st = lib.spec_kv_commit(B, Hkv, D, _dtype_code(k_cache), ctypes.byref(kv), _ptr(cache_len),
+                            _ptr(pad), pad.stride(0), ctypes.byref(tkv), tree_k.shape[2],
+                            _ptr(accept_len), _ptr(accept_path), accept_path.shape[1],
+                            _ptr(n_appended), _ptr(workspace), workspace.numel(), _stream(k_cache))
+    _check(st)
+    return n_appended
 
 
 def spec_device_status(workspace: torch.Tensor) -> int:

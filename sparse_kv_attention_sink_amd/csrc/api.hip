@@ -494,6 +494,66 @@ spec_status spec_accept_greedy(int32_t batch, int32_t n_nodes, int32_t vocab, co
   return SPEC_OK;
 }
 
+spec_status spec_kv_commit(int32_t batch, int32_t n_kv_heads, int32_t head_dim, int32_t dtype,
+                           const spec_kv_mut* cache, int32_t* cache_len, uint8_t* pad,
+                           int64_t pad_stride_b, const spec_kv* tree, int32_t n_nodes,
+                           const int32_t* accept_len, const int32_t* accept_path,
+                           int32_t max_depth, int32_t* n_appended_or_null, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  const spec_dims d{batch, n_kv_heads, n_kv_heads, head_dim, dtype, 1.f};
+  spec_status st = check_dims(&d);
+  if (st != SPEC_OK) return st;
+  if (n_nodes < 1 || n_nodes > kMaxNodes)
+    return fail(n_nodes > kMaxNodes ? SPEC_E_UNSUPPORTED : SPEC_E_INVALID, "n_nodes %d outside [1, 64]", n_nodes);
+  if (max_depth < 1) return fail(SPEC_E_INVALID, "max_depth %d < 1", max_depth);
+  if (batch == 0) return SPEC_OK;   // nothing to read or write; pointers may be NULL
+  if (cache == nullptr) return fail(SPEC_E_INVALID, "cache is NULL");
+  const spec_kv c{cache->k, cache->v, cache->stride_b, cache->stride_h, cache->stride_t, cache->capacity};
+  if ((st = check_kv(&c, &d, "cache", true)) != SPEC_OK) return st;
+  if ((st = check_kv(tree, &d, "tree", false)) != SPEC_OK) return st;
+  if (cache_len == nullptr || pad == nullptr || accept_len == nullptr || accept_path == nullptr)
+    return fail(SPEC_E_INVALID, "a required pointer is NULL");
+  if (!aligned(cache_len, 4) || !aligned(accept_len, 4) || !aligned(accept_path, 4) ||
+      (n_appended_or_null != nullptr && !aligned(n_appended_or_null, 4)))
+    return fail(SPEC_E_INVALID, "int32 arrays must be 4-byte aligned");
+  if (pad_stride_b < cache->capacity)
+    return fail(SPEC_E_INVALID, "pad_stride_b %lld < capacity %d", (long long)pad_stride_b, cache->capacity);
+  if (workspace == nullptr || workspace_bytes < kHeaderBytes)
+    return fail(SPEC_E_WORKSPACE, "workspace of %zu bytes needed (got %zu)", kHeaderBytes,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  if (!aligned(workspace, 256)) return fail(SPEC_E_INVALID, "workspace must be 256-byte aligned");
+  const int64_t es = esize(dtype);
+  CommitArgs a;
+  a.k = static_cast<char*>(cache->k);
+  a.v = static_cast<char*>(cache->v);
+  a.c_sb = cache->stride_b * es;
+  a.c_sh = cache->stride_h * es;
+  a.c_st = cache->stride_t * es;
+  a.tk = static_cast<const char*>(tree->k);
+  a.tv = static_cast<const char*>(tree->v);
+  a.t_sb = tree->stride_b * es;
+  a.t_sh = tree->stride_h * es;
+  a.t_st = tree->stride_t * es;
+  a.batch = batch;
+  a.n_kv_heads = n_kv_heads;
+  a.row_chunks = (int32_t)(head_dim * es / 16);
+  a.capacity = cache->capacity;
+  a.n_nodes = n_nodes;
+  a.max_depth = max_depth;
+  a.cache_len = cache_len;
+  a.pad = pad;
+  a.pad_sb = pad_stride_b;
+  a.accept_len = accept_len;
+  a.accept_path = accept_path;
+  a.n_appended = n_appended_or_null;
+  a.err = static_cast<uint32_t*>(workspace);
+  hipError_t e = launch_kv_commit(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "kv commit launch");
+  return SPEC_OK;
+}
+
+size_t spec_commit_workspace_bytes(void) { return kHeaderBytes; }
+
 spec_status spec_device_status(void* workspace, void* stream, uint32_t* bits_or_null) {
   if (workspace == nullptr) return fail(SPEC_E_INVALID, "workspace is NULL");
   hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));

@@ -94,6 +94,24 @@ struct Plan {
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Arguments of the KV commit kernel (byte strides; validated by the caller).
+struct CommitArgs {
+  char* k;
+  char* v;
+  int64_t c_sb, c_sh, c_st;            // cache strides in bytes
+  const char* tk;
+  const char* tv;
+  int64_t t_sb, t_sh, t_st;            // tree strides in bytes
+  int32_t batch, n_kv_heads, row_chunks, capacity, n_nodes, max_depth;
+  int32_t* cache_len;
+  uint8_t* pad;
+  int64_t pad_sb;
+  const int32_t* accept_len;
+  const int32_t* accept_path;
+  int32_t* n_appended;
+  uint32_t* err;
+};
+
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error; arguments were validated.
 hipError_t launch_attn_bf16(const AttnArgs& a, int mode, const Plan& p, hipStream_t st);
@@ -106,5 +124,6 @@ hipError_t launch_accept(int B, int N, int V, const float* logits, const int32_t
                          const int32_t* parents, int64_t parents_sb, int max_depth,
                          int32_t* accept_len, int32_t* accept_path, int32_t* bonus,
                          void* ws, int vsplits, hipStream_t st, uint32_t* err);
+hipError_t launch_kv_commit(const CommitArgs& a, hipStream_t st);
 
 }  // namespace spec

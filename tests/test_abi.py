@@ -27,9 +27,10 @@ def header_functions():
                                  text, flags=re.M)))
 
 
-def test_header_declares_the_three_operations():
+def test_header_declares_the_four_operations():
     fns = header_functions()
-    for name in ("spec_attn_draft_sparse", "spec_attn_verify_tree", "spec_accept_greedy"):
+    for name in ("spec_attn_draft_sparse", "spec_attn_verify_tree", "spec_accept_greedy",
+                 "spec_kv_commit"):
         assert name in fns
 
 
@@ -150,6 +151,45 @@ def test_accept_rejects_bad_pointers(lib):
                                   8, None) == skg.SPEC_E_WORKSPACE
 
 
+def commit(lib, *, B=2, hkv=8, D=128, dtype=skg.SPEC_BF16, cache=None, tree=None, n=5, cl=FAKE,
+           pad=FAKE, pad_sb=4096, al=FAKE, ap=FAKE, md=4, na=None, ws=FAKE, wsb=256):
+    cache = cache or kv()
+    tree = tree or kv(cap=n)
+    return lib.spec_kv_commit(B, hkv, D, dtype, ctypes.byref(cache), cl, pad, pad_sb,
+                              ctypes.byref(tree), n, al, ap, md, na, ws, wsb, None)
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(B=-1), skg.SPEC_E_INVALID),
+    (dict(hkv=0), skg.SPEC_E_INVALID),
+    (dict(D=96), skg.SPEC_E_UNSUPPORTED),
+    (dict(dtype=7), skg.SPEC_E_UNSUPPORTED),
+    (dict(n=0), skg.SPEC_E_INVALID),
+    (dict(n=65), skg.SPEC_E_UNSUPPORTED),
+    (dict(md=0), skg.SPEC_E_INVALID),
+    (dict(cl=None), skg.SPEC_E_INVALID),
+    (dict(pad=None), skg.SPEC_E_INVALID),
+    (dict(al=None), skg.SPEC_E_INVALID),
+    (dict(ap=None), skg.SPEC_E_INVALID),
+    (dict(cl=FAKE + 2), skg.SPEC_E_INVALID),
+    (dict(na=FAKE + 2), skg.SPEC_E_INVALID),
+    (dict(pad_sb=4095), skg.SPEC_E_INVALID),
+    (dict(cache=kv(stride_t=64)), skg.SPEC_E_INVALID),
+    (dict(cache=kv(ptr=FAKE + 8)), skg.SPEC_E_INVALID),
+    (dict(tree=kv(cap=5, ptr=FAKE + 4)), skg.SPEC_E_INVALID),
+    (dict(ws=None), skg.SPEC_E_WORKSPACE),
+    (dict(wsb=16), skg.SPEC_E_WORKSPACE),
+    (dict(ws=FAKE + 16), skg.SPEC_E_INVALID),
+])
+def test_commit_rejects_bad_arguments(lib, bad, status):
+    assert commit(lib, **bad) == status
+    assert lib.spec_last_error()
+
+
+def test_commit_workspace_is_the_error_word(lib):
+    assert lib.spec_commit_workspace_bytes() == 256
+
+
 def test_device_status_rejects_null(lib):
     assert lib.spec_device_status(None, None, None) == skg.SPEC_E_INVALID
 
@@ -160,6 +200,7 @@ def test_empty_batch_is_a_no_op(lib):
     assert verify(lib, dims(B=0)) == skg.SPEC_OK
     assert lib.spec_accept_greedy(0, 4, 100, FAKE, FAKE, FAKE, 0, 4, FAKE, FAKE, FAKE, FAKE,
                                   1 << 30, None) == skg.SPEC_OK
+    assert commit(lib, B=0) == skg.SPEC_OK
 
 
 def test_binding_fails_loudly_without_library(tmp_path):
