@@ -70,6 +70,15 @@ def accept_bytes(B, N, V):
 
 # ------------------------------------------------------------ 1M workload
 
+def prerecord(events, torch):
+    """Record every event once outside the measured pass: a timing event
+    creates its device event at its first record, which costs far more than
+    a later record."""
+    for e in events:
+        e.record()
+    torch.cuda.synchronize()
+
+
 def run_1m(args, torch, skg):
     import synth.device_gen as dg
     dev = torch.device("cuda:0")
@@ -132,18 +141,29 @@ def run_1m(args, torch, skg):
     for w in (ws_v, ws_c, ws_f, ws_a):
         assert skg.spec_device_status(w) == 0, "device range error during warmup"
 
-    marks = [[[ev() for _ in range(4)] for _ in layers] for _ in range(args.steps)]
+    # The timed loop records only its two bracketing events: an event recorded
+    # between two kernels idles the GPU for about 5 us, so the per-call
+    # breakdown comes from a second, instrumented pass over the same steps.
     start, stop = ev(), ev()
     torch.cuda.synchronize()
     start.record()
     t_wall = time.perf_counter()
-    for k in range(args.steps):
-        step(marks[k])
+    for _ in range(args.steps):
+        step()
     stop.record()
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
-    ms_total = start.elapsed_time(stop)
-    ms_step = ms_total / args.steps
+    ms_step = start.elapsed_time(stop) / args.steps
+
+    marks = [[[ev() for _ in range(4)] for _ in layers] for _ in range(args.steps)]
+    prerecord([e for st in marks for m in st for e in m], torch)
+    a, b = ev(), ev()
+    a.record()
+    for k in range(args.steps):
+        step(marks[k])
+    b.record()
+    torch.cuda.synchronize()
+    ms_step_marked = a.elapsed_time(b) / args.steps
 
     t_verify = [m[0].elapsed_time(m[1]) for st in marks for m in st]
     t_ctx = [m[1].elapsed_time(m[2]) for st in marks for m in st]
@@ -152,7 +172,7 @@ def run_1m(args, torch, skg):
     per_step_verify = sum(t_verify) / args.steps
     per_step_ctx = sum(t_ctx) / args.steps
     per_step_fwd = sum(t_fwd) * CHAIN / args.steps
-    t_acc = max(ms_step - per_step_verify - per_step_ctx - per_step_fwd, 0.0)
+    t_acc = max(ms_step_marked - per_step_verify - per_step_ctx - per_step_fwd, 0.0)
 
     vb = verify_bytes(1, L1M, CHAIN)
     cb = draft_bytes(1, L1M, CHAIN, window_view_len(L1M, CHAIN, SINK, WINDOW))
@@ -166,7 +186,7 @@ def run_1m(args, torch, skg):
     fwd_gbs = fb / (sum(t_fwd) / len(t_fwd) * 1e-3) / 1e9
     res = dict(
         ms_step=ms_step, gbs=gbs, steps_per_s=1e3 / ms_step, step_bytes=step_bytes,
-        wall_ms_per_step=t_wall * 1e3 / args.steps,
+        wall_ms_per_step=t_wall * 1e3 / args.steps, ms_step_with_call_marks=ms_step_marked,
         components_ms=dict(t_verify=per_step_verify, t_ctx_draft=per_step_ctx,
                            t_fwd_draft=per_step_fwd, t_accept_and_gaps=t_acc,
                            verify_per_layer=v_avg_ms,
@@ -238,14 +258,21 @@ def run_16k(args, torch, skg):
         for i in range(2):
             step(i)
         torch.cuda.synchronize()
-        marks = [[ev() for _ in range(4)] for _ in range(reps * ROT // 4)]
+        n_steps = reps * ROT // 4
         a, b = ev(), ev()
         a.record()
-        for i, m in enumerate(marks):
-            step(i * 5, m)
+        for i in range(n_steps):
+            step(i * 5)
         b.record()
         torch.cuda.synchronize()
-        ms_step = a.elapsed_time(b) / len(marks)
+        ms_step = a.elapsed_time(b) / n_steps
+        # per-call breakdown from an instrumented pass (events between kernels
+        # idle the GPU for a few microseconds each)
+        marks = [[ev() for _ in range(4)] for _ in range(n_steps)]
+        prerecord([e for m in marks for e in m], torch)
+        for i, m in enumerate(marks):
+            step(i * 5, m)
+        torch.cuda.synchronize()
         tv_ms = sum(m[0].elapsed_time(m[1]) for m in marks) / len(marks)
         td_ms = sum(m[1].elapsed_time(m[2]) for m in marks) / len(marks) / 4
         ta_ms = sum(m[2].elapsed_time(m[3]) for m in marks) / len(marks)
@@ -265,6 +292,67 @@ def run_16k(args, torch, skg):
     del kvs
     torch.cuda.empty_cache()
     return out
+
+
+# ------------------------------------------------------------ KV commit
+
+def run_commit(torch, skg, *, B, L, widths, depths, seed, reps=60):
+    """Time the commit of accepted paths (the step after acceptance) on a
+    batch of B caches holding L tokens each: a tree of the given widths, one
+    accepted root path per sequence of the given depth, back-to-back calls
+    (each appends P = 1 + max depth slots, so the capacity leaves room for
+    all of them)."""
+    import numpy as np
+    import synth
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(seed)
+    tree = synth.layered_tree(rng, widths)
+    N, P = tree.n, 1 + max(depths)
+    cap = L + (reps + 8) * P
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    k = torch.randn((B, HKV, cap, D), generator=g, device=dev).to(torch.bfloat16)
+    v = torch.randn((B, HKV, cap, D), generator=g, device=dev).to(torch.bfloat16)
+    tk = torch.randn((B, HKV, N, D), generator=g, device=dev).to(torch.bfloat16)
+    tv = torch.randn((B, HKV, N, D), generator=g, device=dev).to(torch.bfloat16)
+    maxd = int(tree.depth.max()) + 1
+    path = np.full((B, maxd), -1, dtype=np.int32)
+    for b, d in enumerate(depths):
+        if d:
+            node = int(rng.choice(np.nonzero(tree.depth == d - 1)[0]))
+            p = []
+            while node >= 0:
+                p.append(node)
+                node = int(tree.parents[node])
+            path[b, :d] = p[::-1]
+    alen = torch.tensor(depths, dtype=torch.int32, device=dev)
+    apath = torch.from_numpy(path).to(dev)
+    cl = torch.full((B,), L, dtype=torch.int32, device=dev)
+    pad = torch.zeros((B, cap), dtype=torch.uint8, device=dev)
+    ws = skg.new_workspace(skg.commit_workspace_bytes(), dev)
+    n_out = torch.empty(1, dtype=torch.int32, device=dev)
+    call = lambda: skg.spec_kv_commit(k, v, cl, pad, tk, tv, alen, apath, n_appended=n_out,  # noqa: E731
+                                      workspace=ws)
+    for _ in range(4):
+        call()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    prerecord([a, b], torch)
+    # A few-kernel call costs the host more than the device: park the stream
+    # on a spin long enough for the host to queue every timed call, so the
+    # events measure the device's back-to-back time.
+    torch.cuda._sleep(int(2.5e6 + reps * 1.5e5))
+    a.record()
+    for _ in range(reps):
+        call()
+    b.record()
+    torch.cuda.synchronize()
+    assert skg.spec_device_status(ws) == 0
+    us = a.elapsed_time(b) / reps * 1e3
+    moved = 2 * sum(depths) * HKV * 2 * D * 2 + B * P
+    return dict(us_per_call=round(us, 2), batch=B, context=L, tree_nodes=N,
+                accept_len=list(depths), appended_slots=P, bytes_moved_per_call=moved,
+                gbs=round(moved / (us * 1e-6) / 1e9, 1))
 
 
 # ------------------------------------------------------------ CPU baseline
@@ -414,6 +502,13 @@ def main():
     del layers
     torch.cuda.empty_cache()
     r16 = None if args.skip_16k else run_16k(args, torch, skg)
+    commit = {
+        "16k_batch8_tree64": run_commit(torch, skg, B=8, L=16384, widths=(10, 18, 18, 18),
+                                        depths=[4, 3, 2, 1, 0, 4, 2, 3], seed=8300),
+        "1m_chain3": run_commit(torch, skg, B=1, L=L1M, widths=(1, 1, 1), depths=[3], seed=8301),
+    }
+    log(f"[bench] kv commit: {commit['16k_batch8_tree64']['us_per_call']} us (16K batch 8), "
+        f"{commit['1m_chain3']['us_per_call']} us (1M chain 3)")
 
     v_ms = r1m["verify_avg_ms"]
     achieved = r1m["verify_bytes_per_launch"] / (v_ms * 1e-3) / 1e9
@@ -447,6 +542,7 @@ def main():
                      "avg_launch_ms": round(v_ms, 4)},
         "cpu_baseline": cpu,
         "ctx16k": r16,
+        "kv_commit": commit,
     }
     print(json.dumps(line), flush=True)
 
