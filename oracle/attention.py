@@ -52,7 +52,11 @@ def draft_view(L_b: int, n_q: int, t: int, *, n_sink: int | None = None,
     and including the query itself, each position counted once.
 
     Budget mode (BudgetDraft review, abstract): the caller's list of selected
-    positions, restricted to the causal prefix; a listed position outside
+    positions, restricted to the causal prefix.  An entry of -1 is padding
+    and selects nothing, so lists of one fixed length can describe views of
+    different sizes (a sequence shorter than the budget lists all of its
+    positions, as SpecPV section 3.3 falls back to the whole cache when the
+    sequence is shorter than the partial budget); any other position outside
     ``[0, L_b)`` is an input error.
     """
     e = L_b - n_q + t + 1
@@ -61,6 +65,7 @@ def draft_view(L_b: int, n_q: int, t: int, *, n_sink: int | None = None,
         recent = set(range(max(0, e - window), e))
         return np.array(sorted(sink | recent), dtype=np.int64)
     lst = np.asarray(idx_list, dtype=np.int64)
+    lst = lst[lst != -1]
     if ((lst < 0) | (lst >= L_b)).any():
         raise IndexError("budget index outside [0, cache_len)")
     return lst[lst < e]

@@ -65,6 +65,24 @@ def test_gather_of_every_position_equals_full_attention():
     np.testing.assert_allclose(out[0], ref.transpose(1, 0, 2), rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("T", [1, 3])
+def test_padded_gather_of_a_short_sequence_equals_full_attention(T):
+    """A fixed-length list for a sequence shorter than the budget: every
+    position once, -1 entries scattered in between.  The -1 entries select
+    nothing, so the result is full causal attention (SDPA)."""
+    c = small_case(15, B=1, lens=[23], T=T, L=37)
+    rng = np.random.default_rng(15)
+    lst = np.concatenate([np.arange(23), np.full(17, -1)]).astype(np.int32)
+    idx = lst[rng.permutation(len(lst))][None, None, :]
+    out, _ = oracle.draft_attn_ref(c.q, c.k, c.v, c.cache_len, scale=c.scale, idx=idx)
+    mask = np.zeros((T, 23), dtype=bool)
+    for t in range(T):
+        mask[t, :23 - T + t + 1] = True
+    q = oracle.as_f64(c.q[0]).transpose(1, 0, 2)
+    ref = sdpa(q, oracle.as_f64(c.k[0, :, :23]), oracle.as_f64(c.v[0, :, :23]), mask, c.scale)
+    np.testing.assert_allclose(out[0], ref.transpose(1, 0, 2), rtol=0, atol=1e-12)
+
+
 def test_window_views_match_hand_enumeration():
     with open(os.path.join(GOLDEN, "draft_window_views.json")) as f:
         fx = json.load(f)
@@ -166,11 +184,13 @@ def test_empty_view_row_is_zero_with_minus_inf_lse():
     assert np.all(np.isfinite(lse[0, 1]))
 
 
-def test_budget_index_out_of_range_is_an_error():
+@pytest.mark.parametrize("bad", [20, -2])
+def test_budget_index_out_of_range_is_an_error(bad):
+    """Only -1 is padding; every other position outside [0, L) is an error."""
     c = small_case(19, B=1, lens=[20])
     with pytest.raises(IndexError):
         oracle.draft_attn_ref(c.q, c.k, c.v, c.cache_len, scale=c.scale,
-                              idx=np.array([[[20]]], dtype=np.int32))
+                              idx=np.array([[[3, bad]]], dtype=np.int32))
 
 
 # --------------------------------------------------------------- tree helpers
