@@ -141,8 +141,11 @@ typedef struct {
  * Budget mode (idx != NULL): query t attends to the listed positions
  * idx[b][h'][0..budget) that are < e_t, with h' = kv head (idx_stride_h > 0)
  * or 0 for every head (idx_stride_h == 0).  Duplicates count as often as
- * listed.  A listed value outside [0, cache_len[b]) raises SPEC_DEV_INDEX
- * and poisons that (b, kv head)'s outputs with NaN.  A row that sees no
+ * listed.  An entry of -1 is padding and selects nothing, so one list length
+ * serves views of different sizes ([PV] section 3.3: a sequence shorter than
+ * the budget uses its whole cache).  Any other value outside
+ * [0, cache_len[b]) raises SPEC_DEV_INDEX and poisons that (b, kv head)'s
+ * outputs with NaN.  A row that sees no
  * position gets out = 0 and lse = -inf.  idx is int32, 4-byte aligned.
  *
  * out [B][Tq][Hq][D] (dtype), lse [B][Tq][Hq] fp32 natural-log sum-exp of

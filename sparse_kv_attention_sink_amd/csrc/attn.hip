@@ -321,7 +321,10 @@ void attn_bf16_kernel(AttnArgs a) {
                 SB = Ge::SB, RPI = Ge::RPI;
 
   __shared__ __attribute__((aligned(1024))) uint8_t ring[Cf::RING];
-  __shared__ uint32_t padbits_s[MODE == kVerify ? kMaxPadWords : 1];
+  // per-tile bits of keys to skip: pad slots (verify), -1 list entries (gather)
+  __shared__ uint32_t padbits_s[MODE == kVerify        ? kMaxPadWords
+                                : MODE == kDraftGather ? kMaxGatherKeys / kTileKeys
+                                                       : 1];
   __shared__ int32_t idx_s[MODE == kDraftGather ? kMaxGatherKeys : 1];
   __shared__ int32_t par_s[MODE == kVerify ? kMaxNodes : 1];
   __shared__ int32_t dep_s[MODE == kVerify ? kMaxNodes : 1];
@@ -441,11 +444,19 @@ void attn_bf16_kernel(AttnArgs a) {
     const int v_end = min(t1 * kTileKeys, n_view);
     const int cnt = max(0, v_end - t0 * kTileKeys);
     const int32_t* ib = a.idx + b * a.idx_sb + g * a.idx_sh + t0 * kTileKeys;
+    // -1 entries are padding: they stage row 0 (always addressable) and a
+    // set bit in their tile's skip word, one ballot per 64 entries
     bool bi = false;
-    for (int i = tid; i < cnt; i += 256) {
-      const int j = ib[i];
-      idx_s[i] = j;
-      bi |= (j < 0 || j >= L);
+    for (int i0 = 0; i0 < cnt; i0 += 256) {
+      const int i = i0 + tid;
+      const int j = i < cnt ? ib[i] : 0;
+      if (i < cnt) idx_s[i] = j == -1 ? 0 : j;
+      bi |= (j < -1 || j >= L);
+      const uint64_t skip = __ballot(i < cnt && j == -1);
+      if ((tid & 63) == 0 && i < cnt) {
+        padbits_s[i / kTileKeys] = (uint32_t)skip;
+        if (i + kTileKeys < cnt) padbits_s[i / kTileKeys + 1] = (uint32_t)(skip >> 32);
+      }
     }
     const bool bad_idx = __syncthreads_or(bi);
     if (bad_idx && tid == 0) raise_error(a.err, SPEC_DEV_INDEX);
@@ -635,6 +646,8 @@ void attn_bf16_kernel(AttnArgs a) {
     uint32_t pw = 0u;
     if constexpr (MODE == kVerify) {
       if (!tree_tile && pad_ptr != nullptr) pw = __builtin_amdgcn_readfirstlane(padbits_s[t - t0]);
+    } else if constexpr (MODE == kDraftGather) {
+      pw = __builtin_amdgcn_readfirstlane(padbits_s[t - t0]);
     }
     const bool full = !tree_tile && (t + 1) * kTileKeys <= n_view && !row_masks && pw == 0u;
 
@@ -667,19 +680,11 @@ void attn_bf16_kernel(AttnArgs a) {
     // Visibility of this lane's 8 keys, local index e = h*4 + i, tile key
     // h*16 + q4*4 + i.  `full` tiles (every key visible to every row) skip it.
     uint32_t kmask = 0xffu;
-    if constexpr (MODE == kVerify) {
-      if (!tree_tile && !full) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int kk = (e >> 2) * 16 + q4 * 4 + (e & 3);
-          if (t * kTileKeys + kk >= n_view || ((pw >> kk) & 1u)) kmask &= ~(1u << e);
-        }
-      }
-    } else if (!full) {
+    if (!tree_tile && !full) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int kk = (e >> 2) * 16 + q4 * 4 + (e & 3);
-        if (t * kTileKeys + kk >= n_view) kmask &= ~(1u << e);
+        if (t * kTileKeys + kk >= n_view || ((pw >> kk) & 1u)) kmask &= ~(1u << e);
       }
     }
     int jpos[8];

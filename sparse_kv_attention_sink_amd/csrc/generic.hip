@@ -161,7 +161,9 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
         vrow = vc + (int64_t)j * a.kt;
       } else if (MODE == kDraftGather) {
         const int j = a.idx[b * a.idx_sb + g * a.idx_sh + pos];
-        if (j < 0 || j >= L) {
+        if (j == -1) {          // padding entry: selects nothing
+          vis = false;
+        } else if (j < 0 || j >= L) {
           idx_bad = true;
           vis = false;
         } else {

@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import synth
-from helpers import assert_close, dev, host64
+from helpers import assert_close, assert_lse_close, dev, host64
 
 pytestmark = pytest.mark.gpu
 
@@ -83,6 +83,83 @@ def test_budget_draft_never_reads_unlisted_positions():
     ref, _ = oracle.draft_attn_ref(case.q, case.k, case.v, case.cache_len, scale=case.scale,
                                    idx=idx)
     assert_close(host64(out), ref, "bf16", "budget sentinel")
+
+
+@pytest.mark.parametrize("T", [1, 3])
+def test_padding_entries_of_a_budget_list_select_nothing(T):
+    """-1 entries scattered through fixed-length lists, including a run
+    that fills whole 32-key tiles: the result equals the oracle, and
+    sentinels on every unlisted slot (row 0 included, the row that padding
+    entries stage) never leak."""
+    case = small_case(51 + T, T=T)
+    rng = np.random.default_rng(51)
+    budget = 224
+    idx = np.full((case.B, 1, budget), -1, dtype=np.int32)
+    hidden = np.ones((case.B, case.L_cap), dtype=bool)
+    for b, n in enumerate((120, 60)):
+        pos = np.sort(rng.choice(np.arange(1, int(case.cache_len[b])), n, replace=False))
+        slots = np.sort(rng.choice(np.r_[0:64, 128:budget], n, replace=False))   # [64, 128) stays -1
+        idx[b, 0, slots] = pos
+        hidden[b, pos] = False
+    plant_sentinels(case, hidden)
+    out, lse = skg.spec_attn_draft_sparse(dev(case.q), dev(case.k), dev(case.v),
+                                          dev(case.cache_len), idx=dev(idx))
+    ref, lse_ref = oracle.draft_attn_ref(case.q, case.k, case.v, case.cache_len,
+                                         scale=case.scale, idx=idx)
+    assert_close(host64(out), ref, "bf16", f"padded budget T={T}")
+    assert_lse_close(lse.cpu().numpy().astype(np.float64), lse_ref, 1e-3, "padded budget lse")
+
+
+def test_padded_per_head_lists_and_an_all_padding_head():
+    case = small_case(55)
+    rng = np.random.default_rng(55)
+    budget = 96
+    idx = np.full((case.B, case.Hkv, budget), -1, dtype=np.int32)
+    for b in range(case.B):
+        for g in range(case.Hkv):
+            if (b, g) == (1, 1):
+                continue                                   # nothing listed at all
+            n = int(rng.integers(1, budget))
+            idx[b, g, rng.choice(budget, n, replace=False)] = rng.choice(
+                int(case.cache_len[b]), n, replace=False)
+    out, lse = skg.spec_attn_draft_sparse(dev(case.q), dev(case.k), dev(case.v),
+                                          dev(case.cache_len), idx=dev(idx))
+    ref, lse_ref = oracle.draft_attn_ref(case.q, case.k, case.v, case.cache_len,
+                                         scale=case.scale, idx=idx)
+    got = host64(out)
+    G = case.Hq // case.Hkv
+    assert np.all(got[1, :, G:2 * G] == 0)
+    assert np.all(np.isneginf(lse.cpu().numpy()[1, :, G:2 * G]))
+    assert_close(got, ref, "bf16", "padded per-head lists")
+    assert_lse_close(lse.cpu().numpy().astype(np.float64), lse_ref, 1e-3, "padded lse")
+
+
+def test_padded_budget_list_fp32_path():
+    case = synth.make_attn_case(57, B=2, Hq=2, Hkv=1, D=64, L_cap=300, T=2,
+                                cache_len=[300, 140], dtype="f32")
+    rng = np.random.default_rng(57)
+    idx = np.full((2, 1, 150), -1, dtype=np.int32)
+    idx[0, 0, rng.choice(150, 100, replace=False)] = rng.choice(300, 100, replace=False)
+    idx[1, 0, rng.choice(150, 140, replace=False)] = np.arange(140)
+    out, _ = skg.spec_attn_draft_sparse(dev(case.q), dev(case.k), dev(case.v),
+                                        dev(case.cache_len), idx=dev(idx), scale=case.scale)
+    ref, _ = oracle.draft_attn_ref(case.q, case.k, case.v, case.cache_len, scale=case.scale,
+                                   idx=idx)
+    assert_close(host64(out), ref, "f32", "padded budget fp32")
+
+
+def test_negative_budget_entry_other_than_padding_is_an_error():
+    case = small_case(59)
+    idx = np.tile(np.arange(40, dtype=np.int32), (case.B, 1, 1))
+    idx[0, 0, 5] = -1                                  # padding: fine
+    idx[1, 0, 9] = -2                                  # not padding: an error
+    dims = skg.make_dims(case.B, case.Hq, case.Hkv, case.D, skg.SPEC_BF16)
+    ws = skg.new_workspace(skg.draft_workspace_bytes(dims, 1, 40), "cuda")
+    out, _ = skg.spec_attn_draft_sparse(dev(case.q), dev(case.k), dev(case.v),
+                                        dev(case.cache_len), idx=dev(idx), workspace=ws)
+    assert skg.spec_device_status(ws) == skg.SPEC_DEV_INDEX
+    got = host64(out)
+    assert np.all(np.isnan(got[1])) and np.all(np.isfinite(got[0]))
 
 
 def test_verify_never_reads_pads_or_slots_past_the_cache():
