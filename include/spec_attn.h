@@ -2,7 +2,7 @@
  * spec_attn.h -- C ABI of libspecattn, the attention hot path of long-context
  * speculative decoding on AMD Instinct MI355X (gfx950).
  *
- * Four operations, each a set of HIP kernels launched asynchronously on the
+ * The operations, each a set of HIP kernels launched asynchronously on the
  * caller's stream:
  *
  *   spec_attn_draft_sparse  draft-phase attention over a sparse view of the KV
@@ -15,6 +15,9 @@
  *                           the longest accepted root path and the bonus token.
  *   spec_kv_commit          append the accepted path's K/V to the cache,
  *                           padding the batch to one uniform length.
+ *   spec_block_means,       budget selection: block summaries of the keys,
+ *   spec_select_blocks      then a budget list of sink, best-scoring blocks
+ *                           and window for the draft's budget mode.
  *
  * Conventions for every call
  *   - Tensor arguments are DEVICE pointers owned by the caller.  The library
@@ -53,8 +56,9 @@
  *   [SM] "SpecMemo: Speculative Decoding is in Your Pocket" (Pith review),
  *        "What carries the argument" and Figure 9.
  *   [PV] "SpecPV: Improving Self-Speculative Decoding for Long-Context
- *        Generation via Partial Verification", section 4.1 "Metrics" and
- *        section 3.3 "Rectified with Full Verification".
+ *        Generation via Partial Verification", section 3.2 "Partial
+ *        Verification", section 3.3 "Rectified with Full Verification" and
+ *        section 4.1 (its metrics and the setup of its experiments).
  */
 #ifndef SPEC_ATTN_H
 #define SPEC_ATTN_H
@@ -252,6 +256,61 @@ spec_status spec_kv_commit(int32_t batch, int32_t n_kv_heads, int32_t head_dim, 
                            int32_t max_depth, int32_t* n_appended_or_null,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Block summaries for budget selection ([PV] section 3.2: the partial cache
+ * is chosen at the block level of the cache manager; section 4.1: mean
+ * reduction for the retrieval).
+ *
+ * Block c holds the positions [c * block, (c + 1) * block).  For every
+ * c in [first_block, first_block + n_blocks), means[b][h][c][0..D) (fp32,
+ * contiguous [B][Hkv][max_blocks][D], 16-byte aligned) receives the mean of
+ * the keys cache.k[b][h][j] over the positions j of the block below
+ * cache_len[b] whose pad byte is 0 (pad == NULL: no padding), accumulated in
+ * fp32; a block with no such position gets NaN.  Other blocks are not
+ * touched, so a caller can keep a table and refresh only the blocks an
+ * append changed.  cache.v is not read.  cache_len[b] outside
+ * [0, capacity] raises SPEC_DEV_CACHE_LEN and that sequence's blocks get
+ * NaN.  block >= 1; batch and Hkv at most 65535.
+ * Workspace: spec_select_workspace_bytes() bytes (the device error word).
+ */
+spec_status spec_block_means(const spec_dims* dims, const spec_kv* cache, const int32_t* cache_len,
+                             const uint8_t* pad_or_null, int64_t pad_stride_b, int32_t block,
+                             int32_t first_block, int32_t n_blocks, float* means,
+                             int32_t max_blocks, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/*
+ * Budget list by block-mean scoring ([PV] sections 3.2 and 4.1; [BD]
+ * abstract: a sparse KV view under a fixed budget).
+ *
+ * For each (sequence b, KV head h), with L = cache_len[b]:
+ *   - the sink [0, min(n_sink, L)) and the window [max(n_sink, L - window), L)
+ *     are always listed;
+ *   - the candidate blocks are those meeting the middle [n_sink, L - window);
+ *     block c scores (mean of the h's G query heads x n_q_tokens queries of
+ *     q) . means[b][h][c] in fp32 (a block with a NaN mean has no score);
+ *   - the n_select best scores are chosen, ties to the smaller block index
+ *     (all blocks with a score if fewer have one), and each chosen block
+ *     contributes its positions inside the middle;
+ *   - idx[b][h][0..budget) receives the listed positions whose pad byte is 0,
+ *     in increasing order, then -1 entries up to the budget: the list is the
+ *     budget-mode input of spec_attn_draft_sparse (idx_stride_h = budget).
+ * scores_or_null[b][h][0..max_blocks) receives the block scores, NaN for
+ * blocks that are not candidates or have no score.  q is [B][Tq][Hq][D]
+ * (dims->dtype), means as written by spec_block_means for every block below
+ * capacity (max_blocks * block >= capacity; max_blocks <= 8192).
+ * Requirements: budget >= n_sink + window + n_select * block, n_select <=
+ * 2048.  cache_len[b] outside [0, capacity] raises SPEC_DEV_CACHE_LEN and
+ * writes an all -1 list.  Workspace: spec_select_workspace_bytes() bytes.
+ */
+spec_status spec_select_blocks(const spec_dims* dims, const void* q, int32_t n_q_tokens,
+                               const float* means, int32_t max_blocks, int32_t block,
+                               const int32_t* cache_len, int32_t capacity,
+                               const uint8_t* pad_or_null, int64_t pad_stride_b, int32_t n_sink,
+                               int32_t window, int32_t n_select, int32_t* idx, int32_t budget,
+                               float* scores_or_null, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
 /* Workspace sizes in bytes (0 on invalid arguments; see spec_last_error).
  * max_view_len for the draft: min(capacity, n_sink + window + n_q_tokens - 1)
  * in window mode, the budget in budget mode (a larger value is always safe).
@@ -262,6 +321,7 @@ size_t spec_verify_workspace_bytes(const spec_dims* dims, int32_t n_nodes,
                                    int32_t capacity);
 size_t spec_accept_workspace_bytes(int32_t batch, int32_t n_nodes, int32_t vocab);
 size_t spec_commit_workspace_bytes(void);
+size_t spec_select_workspace_bytes(void);
 
 /* Waits for `stream`, reads and clears the device error word of `workspace`.
  * Returns SPEC_OK, SPEC_E_DEVICE_RANGE (bits in *bits_or_null) or

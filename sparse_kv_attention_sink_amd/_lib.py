@@ -34,7 +34,8 @@ SPEC_DEV_COMMIT = 16
 EXPORTED = [
     "spec_attn_draft_sparse", "spec_attn_verify_tree", "spec_accept_greedy", "spec_kv_commit",
     "spec_draft_workspace_bytes", "spec_verify_workspace_bytes", "spec_accept_workspace_bytes",
-    "spec_commit_workspace_bytes",
+    "spec_commit_workspace_bytes", "spec_block_means", "spec_select_blocks",
+    "spec_select_workspace_bytes",
     "spec_device_status", "spec_status_string", "spec_last_error", "spec_abi_version",
 ]
 
@@ -80,6 +81,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.spec_kv_commit.restype = I32
     lib.spec_commit_workspace_bytes.argtypes = []
     lib.spec_commit_workspace_bytes.restype = SZ
+    lib.spec_block_means.argtypes = [P, P, P, P, I64, I32, I32, I32, P, I32, P, SZ, P]
+    lib.spec_block_means.restype = I32
+    lib.spec_select_blocks.argtypes = [P, P, I32, P, I32, I32, P, I32, P, I64, I32, I32, I32, P,
+                                       I32, P, P, SZ, P]
+    lib.spec_select_blocks.restype = I32
+    lib.spec_select_workspace_bytes.argtypes = []
+    lib.spec_select_workspace_bytes.restype = SZ
     lib.spec_draft_workspace_bytes.argtypes = [P, I32, I32]
     lib.spec_draft_workspace_bytes.restype = SZ
     lib.spec_verify_workspace_bytes.argtypes = [P, I32, I32]
@@ -316,6 +324,80 @@ def spec_kv_commit(k_cache, v_cache, cache_len, pad, tree_k, tree_v, accept_len,
                             _ptr(n_appended), _ptr(workspace), workspace.numel(), _stream(k_cache))
     _check(st)
     return n_appended
+
+
+def select_workspace_bytes() -> int:
+    return int(load().spec_select_workspace_bytes())
+
+
+def _pad_arg(pad, B, capacity):
+    if pad is None:
+        return None, 0
+    if pad.dtype != torch.uint8 or pad.dim() != 2 or pad.shape[0] != B or pad.stride(1) != 1 or \
+            pad.shape[1] < capacity:
+        raise ValueError("pad must be uint8 [B, >= L_cap]")
+    return pad, pad.stride(0)
+
+
+def spec_block_means(k_cache, cache_len, block, *, pad=None, first_block=0, n_blocks=None,
+                     means=None, workspace=None):
+    """Mean key of the cache blocks [first_block, first_block + n_blocks)
+    into ``means`` (fp32 ``[B, Hkv, max_blocks, D]``; allocated for the
+    whole capacity when None).  Returns ``means``."""
+    lib = load()
+    _on_gpu(k_cache, cache_len, pad, means)
+    B, Hkv, cap, D = k_cache.shape
+    if cache_len.dtype != torch.int32 or cache_len.numel() != B or not cache_len.is_contiguous():
+        raise ValueError("cache_len must be a contiguous int32 [B] tensor")
+    if means is None:
+        means = torch.full((B, Hkv, -(-cap // block), D), float("nan"), dtype=torch.float32,
+                           device=k_cache.device)
+    if means.dtype != torch.float32 or means.dim() != 4 or not means.is_contiguous() or \
+            tuple(means.shape[:2]) != (B, Hkv) or means.shape[3] != D:
+        raise ValueError("means must be contiguous fp32 [B, Hkv, max_blocks, D]")
+    if n_blocks is None:
+        n_blocks = means.shape[2] - first_block
+    kv = _kv(k_cache, k_cache)
+    pad_t, psb = _pad_arg(pad, B, cap)
+    dims = make_dims(B, Hkv, Hkv, D, _dtype_code(k_cache))
+    if workspace is None:
+        workspace = new_workspace(select_workspace_bytes(), k_cache.device)
+    st = lib.spec_block_means(ctypes.byref(dims), ctypes.byref(kv), _ptr(cache_len), _ptr(pad_t),
+                              psb, block, first_block, n_blocks, _ptr(means), means.shape[2],
+                              _ptr(workspace), workspace.numel(), _stream(k_cache))
+    _check(st)
+    return means
+
+
+def spec_select_blocks(q, means, cache_len, *, block, capacity, n_sink, window, n_select, budget,
+                       pad=None, idx=None, scores=None, want_scores=False, workspace=None):
+    """Budget lists ``[B, Hkv, budget]`` int32 (sink, best-scoring blocks,
+    window; -1 padded) from block means.  Returns (idx, scores or None)."""
+    lib = load()
+    _on_gpu(q, means, cache_len, pad, idx, scores)
+    if q.dim() != 4 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B, Tq, Hq, D] tensor")
+    B, T, Hq, D = q.shape
+    if means.dtype != torch.float32 or means.dim() != 4 or not means.is_contiguous() or \
+            means.shape[0] != B or means.shape[3] != D:
+        raise ValueError("means must be contiguous fp32 [B, Hkv, max_blocks, D]")
+    Hkv, max_blocks = means.shape[1], means.shape[2]
+    if cache_len.dtype != torch.int32 or cache_len.numel() != B or not cache_len.is_contiguous():
+        raise ValueError("cache_len must be a contiguous int32 [B] tensor")
+    pad_t, psb = _pad_arg(pad, B, capacity)
+    if idx is None:
+        idx = torch.empty((B, Hkv, budget), dtype=torch.int32, device=q.device)
+    if scores is None and want_scores:
+        scores = torch.empty((B, Hkv, max_blocks), dtype=torch.float32, device=q.device)
+    dims = make_dims(B, Hq, Hkv, D, _dtype_code(q))
+    if workspace is None:
+        workspace = new_workspace(select_workspace_bytes(), q.device)
+    st = lib.spec_select_blocks(ctypes.byref(dims), _ptr(q), T, _ptr(means), max_blocks, block,
+                                _ptr(cache_len), capacity, _ptr(pad_t), psb, n_sink, window,
+                                n_select, _ptr(idx), budget, _ptr(scores), _ptr(workspace),
+                                workspace.numel(), _stream(q))
+    _check(st)
+    return idx, scores
 
 
 def spec_device_status(workspace: torch.Tensor) -> int:

@@ -554,6 +554,120 @@ spec_status spec_kv_commit(int32_t batch, int32_t n_kv_heads, int32_t head_dim, 
 
 size_t spec_commit_workspace_bytes(void) { return kHeaderBytes; }
 
+spec_status spec_block_means(const spec_dims* dims, const spec_kv* cache, const int32_t* cache_len,
+                             const uint8_t* pad_or_null, int64_t pad_stride_b, int32_t block,
+                             int32_t first_block, int32_t n_blocks, float* means,
+                             int32_t max_blocks, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  spec_status st = check_dims(dims);
+  if (st != SPEC_OK) return st;
+  if (block < 1) return fail(SPEC_E_INVALID, "block %d < 1", block);
+  if (first_block < 0 || n_blocks < 0 || max_blocks < 1 ||
+      (int64_t)first_block + n_blocks > max_blocks)
+    return fail(SPEC_E_INVALID, "need 0 <= first_block, 0 <= n_blocks, first_block + n_blocks <= max_blocks");
+  if (dims->batch > 65535 || dims->n_kv_heads > 65535)
+    return fail(SPEC_E_UNSUPPORTED, "batch and n_kv_heads must be <= 65535");
+  if (dims->batch == 0 || n_blocks == 0) return SPEC_OK;
+  if ((st = check_kv(cache, dims, "cache", true)) != SPEC_OK) return st;
+  if (cache_len == nullptr || means == nullptr) return fail(SPEC_E_INVALID, "a required pointer is NULL");
+  if (!aligned(cache_len, 4) || !aligned(means, 16))
+    return fail(SPEC_E_INVALID, "cache_len must be 4-byte and means 16-byte aligned");
+  if (pad_or_null != nullptr && pad_stride_b < cache->capacity)
+    return fail(SPEC_E_INVALID, "pad_stride_b %lld < capacity %d", (long long)pad_stride_b, cache->capacity);
+  if (workspace == nullptr || workspace_bytes < kHeaderBytes)
+    return fail(SPEC_E_WORKSPACE, "workspace of %zu bytes needed", kHeaderBytes);
+  if (!aligned(workspace, 256)) return fail(SPEC_E_INVALID, "workspace must be 256-byte aligned");
+  const int64_t es = esize(dims->dtype);
+  MeansArgs a;
+  a.k = static_cast<const char*>(cache->k);
+  a.k_sb = cache->stride_b * es;
+  a.k_sh = cache->stride_h * es;
+  a.k_st = cache->stride_t * es;
+  a.bf16 = dims->dtype == SPEC_BF16;
+  a.head_dim = dims->head_dim;
+  a.row_chunks = (int32_t)(dims->head_dim * es / 16);
+  a.batch = dims->batch;
+  a.n_kv_heads = dims->n_kv_heads;
+  a.capacity = cache->capacity;
+  a.block = block;
+  a.first_block = first_block;
+  a.n_blocks = n_blocks;
+  a.max_blocks = max_blocks;
+  a.cache_len = cache_len;
+  a.pad = pad_or_null;
+  a.pad_sb = pad_stride_b;
+  a.means = means;
+  a.err = static_cast<uint32_t*>(workspace);
+  hipError_t e = launch_block_means(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "block means launch");
+  return SPEC_OK;
+}
+
+spec_status spec_select_blocks(const spec_dims* dims, const void* q, int32_t n_q_tokens,
+                               const float* means, int32_t max_blocks, int32_t block,
+                               const int32_t* cache_len, int32_t capacity,
+                               const uint8_t* pad_or_null, int64_t pad_stride_b, int32_t n_sink,
+                               int32_t window, int32_t n_select, int32_t* idx, int32_t budget,
+                               float* scores_or_null, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  spec_status st = check_dims(dims);
+  if (st != SPEC_OK) return st;
+  if (n_q_tokens < 1) return fail(SPEC_E_INVALID, "n_q_tokens %d < 1", n_q_tokens);
+  if (block < 1 || max_blocks < 1 || capacity < 0)
+    return fail(SPEC_E_INVALID, "need block >= 1, max_blocks >= 1, capacity >= 0");
+  if (max_blocks > kMaxSelectBlocks)
+    return fail(SPEC_E_UNSUPPORTED, "max_blocks %d > %d", max_blocks, kMaxSelectBlocks);
+  if ((int64_t)max_blocks * block < capacity)
+    return fail(SPEC_E_INVALID, "max_blocks x block (%lld) does not cover capacity %d",
+                (long long)max_blocks * block, capacity);
+  if (n_sink < 0 || window < 0 || n_select < 0)
+    return fail(SPEC_E_INVALID, "n_sink, window and n_select must be >= 0");
+  if (n_select > kMaxSelect) return fail(SPEC_E_UNSUPPORTED, "n_select %d > %d", n_select, kMaxSelect);
+  if (budget < 1 || (int64_t)budget < (int64_t)n_sink + window + (int64_t)n_select * block)
+    return fail(SPEC_E_INVALID, "budget %d < n_sink + window + n_select x block", budget);
+  if (dims->batch > 65535 || dims->n_kv_heads > 65535)
+    return fail(SPEC_E_UNSUPPORTED, "batch and n_kv_heads must be <= 65535");
+  if (dims->batch == 0) return SPEC_OK;
+  if (q == nullptr || means == nullptr || cache_len == nullptr || idx == nullptr)
+    return fail(SPEC_E_INVALID, "a required pointer is NULL");
+  if (!aligned(q, 16) || !aligned(means, 16)) return fail(SPEC_E_INVALID, "q and means must be 16-byte aligned");
+  if (!aligned(cache_len, 4) || !aligned(idx, 4) || (scores_or_null != nullptr && !aligned(scores_or_null, 4)))
+    return fail(SPEC_E_INVALID, "cache_len, idx and scores must be 4-byte aligned");
+  if (pad_or_null != nullptr && pad_stride_b < capacity)
+    return fail(SPEC_E_INVALID, "pad_stride_b %lld < capacity %d", (long long)pad_stride_b, capacity);
+  if (workspace == nullptr || workspace_bytes < kHeaderBytes)
+    return fail(SPEC_E_WORKSPACE, "workspace of %zu bytes needed", kHeaderBytes);
+  if (!aligned(workspace, 256)) return fail(SPEC_E_INVALID, "workspace must be 256-byte aligned");
+  SelectArgs a;
+  a.q = q;
+  a.bf16 = dims->dtype == SPEC_BF16;
+  a.T = n_q_tokens;
+  a.Hq = dims->n_q_heads;
+  a.G = dims->n_q_heads / dims->n_kv_heads;
+  a.head_dim = dims->head_dim;
+  a.batch = dims->batch;
+  a.n_kv_heads = dims->n_kv_heads;
+  a.capacity = capacity;
+  a.means = means;
+  a.max_blocks = max_blocks;
+  a.block = block;
+  a.n_sink = n_sink;
+  a.window = window;
+  a.n_select = n_select;
+  a.budget = budget;
+  a.cache_len = cache_len;
+  a.pad = pad_or_null;
+  a.pad_sb = pad_stride_b;
+  a.idx = idx;
+  a.scores = scores_or_null;
+  a.err = static_cast<uint32_t*>(workspace);
+  hipError_t e = launch_select_blocks(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "block selection launch");
+  return SPEC_OK;
+}
+
+size_t spec_select_workspace_bytes(void) { return kHeaderBytes; }
+
 spec_status spec_device_status(void* workspace, void* stream, uint32_t* bits_or_null) {
   if (workspace == nullptr) return fail(SPEC_E_INVALID, "workspace is NULL");
   hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));

@@ -30,6 +30,8 @@ constexpr int kMaxPadWords = 1024;             // 32-key pad words one workgroup
 constexpr int kMergeFan = 16;                  // partials one split-merge step reads
 constexpr int kMaxSplits = kMergeFan * kMergeFan;
 constexpr int kChunkTiles = 8;                 // tiles per dynamically taken chunk
+constexpr int kMaxSelectBlocks = 8192;         // candidate blocks one selection scores
+constexpr int kMaxSelect = 2048;               // blocks one selection may choose
 
 enum Mode : int { kDraftWindow = 0, kDraftGather = 1, kVerify = 2 };
 
@@ -112,6 +114,33 @@ struct CommitArgs {
   uint32_t* err;
 };
 
+// Arguments of the block-mean kernel (byte strides; validated by the caller).
+struct MeansArgs {
+  const char* k;
+  int64_t k_sb, k_sh, k_st;
+  int32_t bf16, head_dim, row_chunks, batch, n_kv_heads, capacity;
+  int32_t block, first_block, n_blocks, max_blocks;
+  const int32_t* cache_len;
+  const uint8_t* pad;
+  int64_t pad_sb;
+  float* means;                        // [B][Hkv][max_blocks][D]
+  uint32_t* err;
+};
+
+// Arguments of the block selection kernel.
+struct SelectArgs {
+  const void* q;                       // [B][T][Hq][D]
+  int32_t bf16, T, Hq, G, head_dim, batch, n_kv_heads, capacity;
+  const float* means;                  // [B][Hkv][max_blocks][D]
+  int32_t max_blocks, block, n_sink, window, n_select, budget;
+  const int32_t* cache_len;
+  const uint8_t* pad;
+  int64_t pad_sb;
+  int32_t* idx;                        // [B][Hkv][budget]
+  float* scores;                       // [B][Hkv][max_blocks] or null
+  uint32_t* err;
+};
+
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error; arguments were validated.
 hipError_t launch_attn_bf16(const AttnArgs& a, int mode, const Plan& p, hipStream_t st);
@@ -125,5 +154,7 @@ hipError_t launch_accept(int B, int N, int V, const float* logits, const int32_t
                          int32_t* accept_len, int32_t* accept_path, int32_t* bonus,
                          void* ws, int vsplits, hipStream_t st, uint32_t* err);
 hipError_t launch_kv_commit(const CommitArgs& a, hipStream_t st);
+hipError_t launch_block_means(const MeansArgs& a, hipStream_t st);
+hipError_t launch_select_blocks(const SelectArgs& a, hipStream_t st);
 
 }  // namespace spec

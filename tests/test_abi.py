@@ -190,6 +190,55 @@ def test_commit_workspace_is_the_error_word(lib):
     assert lib.spec_commit_workspace_bytes() == 256
 
 
+def means_call(lib, d, *, cache=None, block=16, first=0, n=4, means=FAKE, max_blocks=256,
+               cl=FAKE, pad=None, pad_sb=0, ws=FAKE, wsb=256):
+    cache = cache or kv()
+    return lib.spec_block_means(ctypes.byref(d), ctypes.byref(cache), cl, pad, pad_sb, block,
+                                first, n, means, max_blocks, ws, wsb, None)
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(block=0), skg.SPEC_E_INVALID),
+    (dict(first=-1), skg.SPEC_E_INVALID),
+    (dict(first=250, n=7), skg.SPEC_E_INVALID),
+    (dict(means=None), skg.SPEC_E_INVALID),
+    (dict(means=FAKE + 4), skg.SPEC_E_INVALID),
+    (dict(cl=None), skg.SPEC_E_INVALID),
+    (dict(pad=FAKE, pad_sb=100), skg.SPEC_E_INVALID),
+    (dict(cache=kv(stride_t=64)), skg.SPEC_E_INVALID),
+    (dict(ws=None), skg.SPEC_E_WORKSPACE),
+    (dict(ws=FAKE + 8), skg.SPEC_E_INVALID),
+])
+def test_block_means_rejects_bad_arguments(lib, bad, status):
+    assert means_call(lib, dims(), **bad) == status
+
+
+def select_call(lib, d, *, q=FAKE, tq=1, means=FAKE, max_blocks=256, block=16, cl=FAKE, cap=4096,
+                pad=None, pad_sb=0, sink=4, win=64, nsel=8, idx=FAKE, budget=196, scores=None,
+                ws=FAKE, wsb=256):
+    return lib.spec_select_blocks(ctypes.byref(d), q, tq, means, max_blocks, block, cl, cap, pad,
+                                  pad_sb, sink, win, nsel, idx, budget, scores, ws, wsb, None)
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(tq=0), skg.SPEC_E_INVALID),
+    (dict(block=0), skg.SPEC_E_INVALID),
+    (dict(max_blocks=255), skg.SPEC_E_INVALID),          # 255 x 16 < 4096
+    (dict(max_blocks=8193, cap=16), skg.SPEC_E_UNSUPPORTED),
+    (dict(nsel=2049, budget=1 << 20), skg.SPEC_E_UNSUPPORTED),
+    (dict(budget=195), skg.SPEC_E_INVALID),              # 4 + 64 + 8 x 16 = 196
+    (dict(sink=-1), skg.SPEC_E_INVALID),
+    (dict(q=None), skg.SPEC_E_INVALID),
+    (dict(q=FAKE + 2), skg.SPEC_E_INVALID),
+    (dict(idx=None), skg.SPEC_E_INVALID),
+    (dict(scores=FAKE + 2), skg.SPEC_E_INVALID),
+    (dict(pad=FAKE, pad_sb=4000), skg.SPEC_E_INVALID),
+    (dict(wsb=4), skg.SPEC_E_WORKSPACE),
+])
+def test_select_blocks_rejects_bad_arguments(lib, bad, status):
+    assert select_call(lib, dims(), **bad) == status
+
+
 def test_device_status_rejects_null(lib):
     assert lib.spec_device_status(None, None, None) == skg.SPEC_E_INVALID
 
@@ -201,6 +250,9 @@ def test_empty_batch_is_a_no_op(lib):
     assert lib.spec_accept_greedy(0, 4, 100, FAKE, FAKE, FAKE, 0, 4, FAKE, FAKE, FAKE, FAKE,
                                   1 << 30, None) == skg.SPEC_OK
     assert commit(lib, B=0) == skg.SPEC_OK
+    assert means_call(lib, dims(B=0)) == skg.SPEC_OK
+    assert select_call(lib, dims(B=0)) == skg.SPEC_OK
+    assert lib.spec_select_workspace_bytes() == 256
 
 
 def test_binding_fails_loudly_without_library(tmp_path):
