@@ -355,6 +355,68 @@ def run_commit(torch, skg, *, B, L, widths, depths, seed, reps=60):
                 gbs=round(moved / (us * 1e-6) / 1e9, 1))
 
 
+# ------------------------------------------------------------ budget selection
+
+def run_select(torch, skg, *, B=8, L=16384, block=16, reps=24, seed=8400):
+    """Time the block-mean table build (every block of a batch of B caches
+    of L tokens) and the block selection per draft budget (window B/2, sink
+    4, as many blocks as the rest holds).  Keys and tables are rotated over
+    enough copies that the Infinity Cache does not serve them."""
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    s = 1.0 / math.sqrt(D)
+    ROTK, ROTM = 4, 16
+    ks = [(torch.randn((B, HKV, L, D), generator=g, device=dev) * s).to(torch.bfloat16)
+          for _ in range(ROTK)]
+    q = (torch.randn((B, 1, HQ, D), generator=g, device=dev) * s).to(torch.bfloat16)
+    cl = torch.full((B,), L, dtype=torch.int32, device=dev)
+    nb = L // block
+    tables = [torch.empty((B, HKV, nb, D), dtype=torch.float32, device=dev) for _ in range(ROTM)]
+    ws = skg.new_workspace(skg.select_workspace_bytes(skg.make_dims(B, HQ, HKV, D, skg.SPEC_BF16),
+                                                      nb), dev)
+    for i, t in enumerate(tables):
+        skg.spec_block_means(ks[i % ROTK], cl, block, means=t, workspace=ws)
+    torch.cuda.synchronize()
+
+    def timed(fn, n):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        prerecord([a, b], torch)
+        torch.cuda._sleep(int(2.5e6 + n * 3e5))      # let the host queue every call first
+        a.record()
+        for i in range(n):
+            fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n * 1e3
+
+    means_us = timed(lambda i: skg.spec_block_means(ks[i % ROTK], cl, block,
+                                                    means=tables[i % ROTM], workspace=ws), reps)
+    means_bytes = B * HKV * L * D * 2 + B * HKV * nb * D * 4
+    out = dict(block=block, batch=B, context=L,
+               means_table_us=round(means_us, 2),
+               means_table_gbs=round(means_bytes / (means_us * 1e-6) / 1e9, 1),
+               means_bytes=means_bytes, select={})
+    for bud in (256, 512, 1024, 2048):
+        win = bud // 2
+        nsel = (bud - 4 - win) // block
+        idx = torch.empty((B, HKV, bud), dtype=torch.int32, device=dev)
+        fn = lambda i: skg.spec_select_blocks(q, tables[i % ROTM], cl, block=block,  # noqa: E731
+                                              capacity=L, n_sink=4, window=win, n_select=nsel,
+                                              budget=bud, idx=idx, workspace=ws)
+        fn(0)
+        us = timed(fn, reps)
+        cand = (L - win - 4 + block - 1) // block
+        sel_bytes = B * HKV * cand * D * 4 + B * HKV * bud * 4
+        out["select"][str(bud)] = dict(n_select=nsel, us_per_call=round(us, 2),
+                                       bytes_per_call=sel_bytes,
+                                       gbs=round(sel_bytes / (us * 1e-6) / 1e9, 1))
+    assert skg.spec_device_status(ws) == 0
+    del ks, tables
+    torch.cuda.empty_cache()
+    return out
+
+
 # ------------------------------------------------------------ CPU baseline
 
 def cpu_baseline(layers, torch, budget_s=12.0):
@@ -509,6 +571,9 @@ def main():
     }
     log(f"[bench] kv commit: {commit['16k_batch8_tree64']['us_per_call']} us (16K batch 8), "
         f"{commit['1m_chain3']['us_per_call']} us (1M chain 3)")
+    select = run_select(torch, skg)
+    log(f"[bench] block means table: {select['means_table_us']} us; selection: "
+        + ", ".join(f"{k} {v['us_per_call']} us" for k, v in select["select"].items()))
 
     v_ms = r1m["verify_avg_ms"]
     achieved = r1m["verify_bytes_per_launch"] / (v_ms * 1e-3) / 1e9
@@ -543,6 +608,7 @@ def main():
         "cpu_baseline": cpu,
         "ctx16k": r16,
         "kv_commit": commit,
+        "budget_select": select,
     }
     print(json.dumps(line), flush=True)
 

@@ -271,7 +271,8 @@ spec_status spec_kv_commit(int32_t batch, int32_t n_kv_heads, int32_t head_dim, 
  * append changed.  cache.v is not read.  cache_len[b] outside
  * [0, capacity] raises SPEC_DEV_CACHE_LEN and that sequence's blocks get
  * NaN.  block >= 1; batch and Hkv at most 65535.
- * Workspace: spec_select_workspace_bytes() bytes (the device error word).
+ * Workspace: at least spec_select_workspace_bytes(dims, 0) bytes (the device
+ * error word).
  */
 spec_status spec_block_means(const spec_dims* dims, const spec_kv* cache, const int32_t* cache_len,
                              const uint8_t* pad_or_null, int64_t pad_stride_b, int32_t block,
@@ -301,7 +302,8 @@ spec_status spec_block_means(const spec_dims* dims, const spec_kv* cache, const 
  * capacity (max_blocks * block >= capacity; max_blocks <= 8192).
  * Requirements: budget >= n_sink + window + n_select * block, n_select <=
  * 2048.  cache_len[b] outside [0, capacity] raises SPEC_DEV_CACHE_LEN and
- * writes an all -1 list.  Workspace: spec_select_workspace_bytes() bytes.
+ * writes an all -1 list.  Workspace: spec_select_workspace_bytes(dims,
+ * max_blocks) bytes (the error word and the block scores).
  */
 spec_status spec_select_blocks(const spec_dims* dims, const void* q, int32_t n_q_tokens,
                                const float* means, int32_t max_blocks, int32_t block,
@@ -321,7 +323,7 @@ size_t spec_verify_workspace_bytes(const spec_dims* dims, int32_t n_nodes,
                                    int32_t capacity);
 size_t spec_accept_workspace_bytes(int32_t batch, int32_t n_nodes, int32_t vocab);
 size_t spec_commit_workspace_bytes(void);
-size_t spec_select_workspace_bytes(void);
+size_t spec_select_workspace_bytes(const spec_dims* dims, int32_t max_blocks);
 
 /* Waits for `stream`, reads and clears the device error word of `workspace`.
  * Returns SPEC_OK, SPEC_E_DEVICE_RANGE (bits in *bits_or_null) or

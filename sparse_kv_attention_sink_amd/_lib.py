@@ -86,7 +86,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.spec_select_blocks.argtypes = [P, P, I32, P, I32, I32, P, I32, P, I64, I32, I32, I32, P,
                                        I32, P, P, SZ, P]
     lib.spec_select_blocks.restype = I32
-    lib.spec_select_workspace_bytes.argtypes = []
+    lib.spec_select_workspace_bytes.argtypes = [P, I32]
     lib.spec_select_workspace_bytes.restype = SZ
     lib.spec_draft_workspace_bytes.argtypes = [P, I32, I32]
     lib.spec_draft_workspace_bytes.restype = SZ
@@ -326,8 +326,8 @@ def spec_kv_commit(k_cache, v_cache, cache_len, pad, tree_k, tree_v, accept_len,
     return n_appended
 
 
-def select_workspace_bytes() -> int:
-    return int(load().spec_select_workspace_bytes())
+def select_workspace_bytes(dims: SpecDims, max_blocks: int = 0) -> int:
+    return int(load().spec_select_workspace_bytes(ctypes.byref(dims), max_blocks))
 
 
 def _pad_arg(pad, B, capacity):
@@ -361,7 +361,7 @@ def spec_block_means(k_cache, cache_len, block, *, pad=None, first_block=0, n_bl
     pad_t, psb = _pad_arg(pad, B, cap)
     dims = make_dims(B, Hkv, Hkv, D, _dtype_code(k_cache))
     if workspace is None:
-        workspace = new_workspace(select_workspace_bytes(), k_cache.device)
+        workspace = new_workspace(select_workspace_bytes(dims), k_cache.device)
     st = lib.spec_block_means(ctypes.byref(dims), ctypes.byref(kv), _ptr(cache_len), _ptr(pad_t),
                               psb, block, first_block, n_blocks, _ptr(means), means.shape[2],
                               _ptr(workspace), workspace.numel(), _stream(k_cache))
@@ -391,7 +391,7 @@ def spec_select_blocks(q, means, cache_len, *, block, capacity, n_sink, window, 
         scores = torch.empty((B, Hkv, max_blocks), dtype=torch.float32, device=q.device)
     dims = make_dims(B, Hq, Hkv, D, _dtype_code(q))
     if workspace is None:
-        workspace = new_workspace(select_workspace_bytes(), q.device)
+        workspace = new_workspace(select_workspace_bytes(dims, max_blocks), q.device)
     st = lib.spec_select_blocks(ctypes.byref(dims), _ptr(q), T, _ptr(means), max_blocks, block,
                                 _ptr(cache_len), capacity, _ptr(pad_t), psb, n_sink, window,
                                 n_select, _ptr(idx), budget, _ptr(scores), _ptr(workspace),

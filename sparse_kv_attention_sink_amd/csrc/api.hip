@@ -204,6 +204,12 @@ int accept_vsplits(int64_t rows, int64_t V) {
   return (int)vs;
 }
 
+// header | fp32 block scores [B][Hkv][max_blocks]
+size_t select_bytes(const spec_dims* d, int32_t max_blocks) {
+  return kHeaderBytes +
+         align_up((size_t)std::max(d->batch, 0) * d->n_kv_heads * std::max(max_blocks, 0) * sizeof(float), 256);
+}
+
 // header | per-sequence arrival counters | (value, index) winner per slice
 size_t accept_bytes(int64_t batch, int64_t rows, int vs) {
   return align_up(kHeaderBytes + align_up((size_t)batch * 4, 256) + (size_t)rows * vs * 8, 256);
@@ -635,8 +641,10 @@ spec_status spec_select_blocks(const spec_dims* dims, const void* q, int32_t n_q
     return fail(SPEC_E_INVALID, "cache_len, idx and scores must be 4-byte aligned");
   if (pad_or_null != nullptr && pad_stride_b < capacity)
     return fail(SPEC_E_INVALID, "pad_stride_b %lld < capacity %d", (long long)pad_stride_b, capacity);
-  if (workspace == nullptr || workspace_bytes < kHeaderBytes)
-    return fail(SPEC_E_WORKSPACE, "workspace of %zu bytes needed", kHeaderBytes);
+  const size_t need = select_bytes(dims, max_blocks);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(SPEC_E_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
   if (!aligned(workspace, 256)) return fail(SPEC_E_INVALID, "workspace must be 256-byte aligned");
   SelectArgs a;
   a.q = q;
@@ -660,13 +668,21 @@ spec_status spec_select_blocks(const spec_dims* dims, const void* q, int32_t n_q
   a.pad_sb = pad_stride_b;
   a.idx = idx;
   a.scores = scores_or_null;
+  a.sc_ws = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + kHeaderBytes);
   a.err = static_cast<uint32_t*>(workspace);
   hipError_t e = launch_select_blocks(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "block selection launch");
   return SPEC_OK;
 }
 
-size_t spec_select_workspace_bytes(void) { return kHeaderBytes; }
+size_t spec_select_workspace_bytes(const spec_dims* dims, int32_t max_blocks) {
+  if (check_dims(dims) != SPEC_OK) return 0;
+  if (max_blocks < 0) {
+    fail(SPEC_E_INVALID, "max_blocks %d < 0", max_blocks);
+    return 0;
+  }
+  return select_bytes(dims, max_blocks);
+}
 
 spec_status spec_device_status(void* workspace, void* stream, uint32_t* bits_or_null) {
   if (workspace == nullptr) return fail(SPEC_E_INVALID, "workspace is NULL");

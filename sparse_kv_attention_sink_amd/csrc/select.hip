@@ -13,10 +13,12 @@
 // (below cache_len, not padding) positions, fp32.  One wavefront per block,
 // rows read as coalesced 16-byte chunks; it streams the K cache once.
 //
-// select_blocks_kernel: one workgroup per (sequence, KV head).  The KV
-// head's queries are averaged; every block that meets the middle between
-// sink and window is scored with (mean query) . (mean key); the n_select
-// best are found exactly by a radix select on order-preserving 32-bit keys
+// score_blocks_kernel: every block that meets the middle between sink and
+// window is scored with (mean query of the KV head) . (mean key), fp32,
+// several workgroups per (sequence, KV head), into the workspace.
+//
+// select_blocks_kernel: one workgroup per (sequence, KV head).  The n_select
+// best scores are found exactly by a radix select on order-preserving 32-bit keys
 // (ties to the smaller block index through a prefix count); the list of sink,
 // chosen blocks and window positions, without pads, is written in increasing
 // order and padded with -1.
@@ -26,7 +28,9 @@ namespace spec {
 
 namespace {
 
-constexpr int kMeanBlocksPerWG = 16;
+constexpr int kMeanBlocksPerWG = 4;   // one block per wavefront
+constexpr int kScoreSteps = 8;
+constexpr int kScoreBlocksPerWG = 16 * kScoreSteps;   // 4 wavefronts x 4 blocks x steps
 
 __global__ __launch_bounds__(256) void block_means_kernel(MeansArgs a) {
   const int b = blockIdx.z, g = blockIdx.y;
@@ -119,10 +123,73 @@ __device__ __forceinline__ int block_exclusive_sum(int x, int* red4, int* total)
   return before + incl - x;
 }
 
+// Candidate blocks of a sequence: those meeting [n_sink, L - window).
+__device__ __forceinline__ void candidate_range(const SelectArgs& a, int L, int* c_lo, int* nc) {
+  const int mid_lo = a.n_sink, mid_hi = L - a.window;
+  *c_lo = 0;
+  *nc = 0;
+  if (mid_hi > mid_lo) {
+    *c_lo = mid_lo / a.block;
+    *nc = min((mid_hi - 1) / a.block + 1, a.max_blocks) - *c_lo;
+  }
+}
+
+// Scores of kScoreBlocksPerWG consecutive blocks of one (sequence, KV head):
+// (mean query) . (mean key) in fp32, NaN for blocks that are not candidates
+// or have no mean.  16 lanes per block, 4 blocks per wavefront step, all of a
+// wavefront's steps in flight together.
+__global__ __launch_bounds__(256) void score_blocks_kernel(SelectArgs a) {
+  const int b = blockIdx.z, g = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  __shared__ float qbar_s[128];
+  const int L = a.cache_len[b];
+  const bool bad = L < 0 || L > a.capacity;
+  const int D = a.head_dim, G = a.G, rows = a.T * G;
+  if (tid < D) {
+    float s = 0.f;
+    for (int r = 0; r < rows; ++r) {
+      const int t = r / G, hh = r % G;
+      const int64_t o = (((int64_t)b * a.T + t) * a.Hq + g * G + hh) * D + tid;
+      s += a.bf16 ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(a.q)[o] << 16)
+                  : reinterpret_cast<const float*>(a.q)[o];
+    }
+    qbar_s[tid] = s / (float)rows;
+  }
+  __syncthreads();
+  int c_lo, nc;
+  candidate_range(a, bad ? 0 : L, &c_lo, &nc);
+  const int c_hi = c_lo + (bad ? 0 : nc);
+  const float* mb = a.means + ((int64_t)b * a.n_kv_heads + g) * a.max_blocks * D;
+  float* so = a.sc_ws + ((int64_t)b * a.n_kv_heads + g) * a.max_blocks;
+  const int per = D / 16, sub = lane & 15;
+  float qv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) qv[e] = e < per ? qbar_s[sub * per + e] : 0.f;
+  const int c0 = blockIdx.x * kScoreBlocksPerWG + wave * 4 + (lane >> 4);
+  f32x4 m[kScoreSteps][2];
+#pragma unroll
+  for (int u = 0; u < kScoreSteps; ++u) {
+    const int c = min(c0 + u * 16, a.max_blocks - 1);
+    const f32x4* src = reinterpret_cast<const f32x4*>(mb + (int64_t)c * D + sub * per);
+    const bool live = c >= c_lo && c < c_hi;
+    m[u][0] = live ? src[0] : f32x4{0.f, 0.f, 0.f, 0.f};
+    m[u][1] = live && per == 8 ? src[1] : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int u = 0; u < kScoreSteps; ++u) {
+    const int c = c0 + u * 16;
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s += m[u][e >> 2][e & 3] * qv[e];
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
+    if (sub == 0 && c < a.max_blocks) so[c] = (c >= c_lo && c < c_hi) ? s : NAN;
+  }
+}
+
 __global__ __launch_bounds__(256) void select_blocks_kernel(SelectArgs a) {
   const int b = blockIdx.y, g = blockIdx.x, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  __shared__ float qbar_s[128];
   __shared__ uint32_t key_s[kMaxSelectBlocks];
   __shared__ int hist_s[256];
   __shared__ int red4[4];
@@ -143,50 +210,14 @@ __global__ __launch_bounds__(256) void select_blocks_kernel(SelectArgs a) {
   }
   const int L = L0;
 
-  // mean query of this KV head (its G heads x T tokens)
-  const int D = a.head_dim, G = a.G, rows = a.T * G;
-  if (tid < D) {
-    float s = 0.f;
-    for (int r = 0; r < rows; ++r) {
-      const int t = r / G, hh = r % G;
-      const int64_t o = (((int64_t)b * a.T + t) * a.Hq + g * G + hh) * D + tid;
-      s += a.bf16 ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(a.q)[o] << 16)
-                  : reinterpret_cast<const float*>(a.q)[o];
-    }
-    qbar_s[tid] = s / (float)rows;
-  }
-
-  // candidate blocks: those meeting the middle [n_sink, L - window)
+  // candidate blocks and their scores (score_blocks_kernel)
   const int mid_lo = a.n_sink, mid_hi = L - a.window;
-  int c_lo = 0, nc = 0;
-  if (mid_hi > mid_lo) {
-    c_lo = mid_lo / a.block;
-    nc = min((mid_hi - 1) / a.block + 1, a.max_blocks) - c_lo;
-  }
-  __syncthreads();
-
-  // scores: 16 lanes per block, 4 blocks per wavefront step
-  const float* mb = a.means + ((int64_t)b * a.n_kv_heads + g) * a.max_blocks * D;
-  const int per = D / 16;                                   // floats per lane (8 or 4)
-  const int sub = lane & 15;
-  for (int i0 = wave * 4; i0 < nc; i0 += 16) {
-    const int i = i0 + (lane >> 4);
-    float s = 0.f;
-    if (i < nc) {
-      const float* m = mb + (int64_t)(c_lo + i) * D + sub * per;
-      for (int e = 0; e < per; ++e) s += m[e] * qbar_s[sub * per + e];
-    }
-#pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
-    if (i < nc && sub == 0) {
-      key_s[i] = score_key(s);
-      if (sc_out != nullptr) sc_out[c_lo + i] = s;
-    }
-  }
-  if (sc_out != nullptr) {
-    for (int c = tid; c < a.max_blocks; c += 256)
-      if (c < c_lo || c >= c_lo + nc) sc_out[c] = NAN;
-  }
+  int c_lo, nc;
+  candidate_range(a, L, &c_lo, &nc);
+  const float* sw = a.sc_ws + ((int64_t)b * a.n_kv_heads + g) * a.max_blocks;
+  for (int i = tid; i < nc; i += 256) key_s[i] = score_key(sw[c_lo + i]);
+  if (sc_out != nullptr)
+    for (int c = tid; c < a.max_blocks; c += 256) sc_out[c] = sw[c];
   __syncthreads();
 
   // how many blocks have a score, and how many are chosen
@@ -346,6 +377,11 @@ hipError_t launch_block_means(const MeansArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_select_blocks(const SelectArgs& a, hipStream_t st) {
+  const unsigned gx = (unsigned)((a.max_blocks + kScoreBlocksPerWG - 1) / kScoreBlocksPerWG);
+  hipLaunchKernelGGL(score_blocks_kernel, dim3(gx, (unsigned)a.n_kv_heads, (unsigned)a.batch),
+                     dim3(256), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(select_blocks_kernel, dim3((unsigned)a.n_kv_heads, (unsigned)a.batch),
                      dim3(256), 0, st, a);
   return hipGetLastError();

@@ -138,6 +138,7 @@ struct SelectArgs {
   int64_t pad_sb;
   int32_t* idx;                        // [B][Hkv][budget]
   float* scores;                       // [B][Hkv][max_blocks] or null
+  float* sc_ws;                        // [B][Hkv][max_blocks] workspace scores
   uint32_t* err;
 };
 

@@ -36,7 +36,11 @@ def run_select(q, k, lens, *, block, n_sink, window, n_select, budget, pad=None,
     kd = dev(k)
     cl = dev(np.asarray(lens, np.int32))
     pd = None if pad is None else dev(pad)
-    ws = ws if ws is not None else skg.new_workspace(skg.select_workspace_bytes(), "cuda")
+    if ws is None:
+        nb = -(-k.shape[2] // block)
+        dims = skg.make_dims(k.shape[0], q.shape[2], k.shape[1], k.shape[3],
+                             skg.SPEC_BF16 if k.dtype == np.uint16 else skg.SPEC_F32)
+        ws = skg.new_workspace(skg.select_workspace_bytes(dims, nb), "cuda")
     means = skg.spec_block_means(kd, cl, block, pad=pd, workspace=ws)
     idx, scores = skg.spec_select_blocks(dev(q), means, cl, block=block, capacity=k.shape[2],
                                          n_sink=n_sink, window=window, n_select=n_select,
