@@ -23,8 +23,9 @@ Sources (page title, then the passage):
 * "SpecPV: Improving Self-Speculative Decoding for Long-Context Generation via
   Partial Verification" -- section 4.1 "Metrics": the accept length may be 0;
   section 3.3: candidates that were not accepted leave the cache once
-  verification is done; section 3.2 and 4.1: the partial cache is chosen
-  block by block with mean reduction.
+  verification is done, and full verification refreshes the partial cache;
+  section 3.2 and 4.1: the partial cache is chosen block by block with mean
+  reduction and is one contiguous KV segment.
 
 Pin status: every public function here is pinned by ``tests/test_oracle_*.py``
 against something other than itself (library SDPA, closed forms, brute force,
@@ -37,8 +38,10 @@ from .attention import (draft_view, draft_attn_ref, tree_depths, tree_ancestors,
 from .accept import argmax_ref, accept_ref, accept_bruteforce
 from .commit import commit_ref
 from .select import block_means_ref, block_scores_ref, select_blocks_ref
+from .partial import gather_ref, verify_mode_ref
 
 __all__ = ["decode_bf16", "as_f64", "draft_view", "draft_attn_ref", "tree_depths",
            "tree_ancestors", "position_ids", "verify_keys", "verify_attn_ref",
            "argmax_ref", "accept_ref", "accept_bruteforce", "commit_ref",
-           "block_means_ref", "block_scores_ref", "select_blocks_ref"]
+           "block_means_ref", "block_scores_ref", "select_blocks_ref", "gather_ref",
+           "verify_mode_ref"]

@@ -16,7 +16,9 @@ Reading of what the pages leave open:
 * A KV head's queries (its G query heads times the Tq query tokens) score
   block c with the mean of their dot products with the block's mean key,
   i.e. (mean query) . (mean key); the softmax scale does not change the
-  order and is left out.
+  order and is left out.  With one list per sequence (``shared``: a cache
+  manager's block holds every head, so a partial cache keeps whole blocks)
+  the mean runs over every KV head's score as well.
 * The list keeps the sink [0, n_sink) and the window
   [max(n_sink, L - window), L) of the draft view (L = cache_len), and
   chooses among the blocks that meet the middle [n_sink, L - window): the
@@ -60,10 +62,12 @@ def candidate_blocks(L: int, block: int, n_sink: int, window: int) -> np.ndarray
     return np.arange(lo // block, (hi - 1) // block + 1)
 
 
-def block_scores_ref(q, means, cache_len, block: int, n_sink: int, window: int) -> np.ndarray:
+def block_scores_ref(q, means, cache_len, block: int, n_sink: int, window: int,
+                     shared: bool = False) -> np.ndarray:
     """Score of every candidate block per (sequence, KV head): ``[B, Hkv,
     n_blocks]`` float64, NaN where a block is not a candidate or has no
-    summary.  ``q`` is ``[B, Tq, Hq, D]``."""
+    summary; with ``shared``, ``[B, 1, n_blocks]``, the mean over the KV
+    heads (NaN if any head has no summary).  ``q`` is ``[B, Tq, Hq, D]``."""
     B, T, Hq, D = q.shape
     Hkv, nb = means.shape[1], means.shape[2]
     G = Hq // Hkv
@@ -74,6 +78,8 @@ def block_scores_ref(q, means, cache_len, block: int, n_sink: int, window: int) 
         for g in range(Hkv):
             qbar = as_f64(q[b, :, g * G:(g + 1) * G]).reshape(-1, D).mean(axis=0)
             sc[b, g, cand] = means[b, g, cand] @ qbar
+    if shared:
+        return sc.mean(axis=1, keepdims=True)
     return sc
 
 
@@ -100,14 +106,16 @@ def select_list(L: int, pad_row, chosen, block: int, n_sink: int, window: int,
 
 
 def select_blocks_ref(q, k, cache_len, *, block: int, n_sink: int, window: int, n_select: int,
-                      budget: int, pad=None, n_blocks: int | None = None):
-    """Budget lists ``[B, Hkv, budget]`` int32 chosen by block-mean scoring,
-    with the scores ``[B, Hkv, n_blocks]`` and the chosen blocks per pair."""
-    B, Hkv = k.shape[0], k.shape[1]
+                      budget: int, pad=None, n_blocks: int | None = None, shared: bool = False):
+    """Budget lists ``[B, Hkv, budget]`` (``[B, 1, budget]`` when shared)
+    int32 chosen by block-mean scoring, with the scores and the chosen blocks
+    per list."""
+    B = k.shape[0]
+    Hkv = 1 if shared else k.shape[1]
     if n_blocks is None:
         n_blocks = -(-k.shape[2] // block)
     means = block_means_ref(k, cache_len, block, n_blocks, pad)
-    sc = block_scores_ref(q, means, cache_len, block, n_sink, window)
+    sc = block_scores_ref(q, means, cache_len, block, n_sink, window, shared)
     idx = np.zeros((B, Hkv, budget), dtype=np.int32)
     chosen = {}
     for b in range(B):

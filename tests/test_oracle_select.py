@@ -176,3 +176,32 @@ def test_lists_skip_pads_stay_sorted_and_within_the_view():
     # sequence 2 (40 tokens) is shorter than sink + window: every non-pad position
     lst = idx[2, 0][idx[2, 0] >= 0]
     np.testing.assert_array_equal(lst, [p for p in range(40) if not pad[2, p]])
+
+
+@pytest.mark.parametrize("seed", range(2))
+def test_shared_score_is_the_mean_over_every_head_of_its_pairwise_scores(seed):
+    """One list per sequence: a block's score is the mean over the KV heads
+    of each head's mean pairwise query-key score (every query head paired
+    with its own KV head)."""
+    c = synth.make_attn_case(6600 + seed, B=1, Hq=8, Hkv=4, D=16, L_cap=64, T=2,
+                             cache_len=[64], dtype="f32", value_scale=1.0)
+    means = oracle.block_means_ref(c.k, c.cache_len, 8, 8)
+    sc = oracle.block_scores_ref(c.q, means, c.cache_len, 8, 4, 8, shared=True)
+    assert sc.shape == (1, 1, 8)
+    for blk in sel.candidate_blocks(64, 8, 4, 8):
+        per_head = []
+        for g in range(4):
+            Q = torch.from_numpy(c.q[0, :, 2 * g:2 * g + 2].reshape(-1, 16).astype(np.float64))
+            K = torch.from_numpy(c.k[0, g, blk * 8:(blk + 1) * 8].astype(np.float64))
+            per_head.append((Q @ K.T).mean().item())
+        assert abs(sc[0, 0, blk] - np.mean(per_head)) <= 1e-12
+
+
+def test_shared_lists_have_one_row_per_sequence():
+    c = synth.make_attn_case(6700, B=2, Hq=8, Hkv=2, D=16, L_cap=200, T=1,
+                             cache_len=[200, 150], dtype="f32")
+    idx, sc, chosen = oracle.select_blocks_ref(c.q, c.k, c.cache_len, block=16, n_sink=4,
+                                               window=32, n_select=3, budget=4 + 32 + 48,
+                                               shared=True)
+    assert idx.shape == (2, 1, 84) and sc.shape[1] == 1
+    assert set(chosen) == {(0, 0), (1, 0)}
