@@ -18,6 +18,9 @@
  *   spec_block_means,       budget selection: block summaries of the keys,
  *   spec_select_blocks      then a budget list of sink, best-scoring blocks
  *                           and window for the draft's budget mode.
+ *   spec_kv_gather,         partial verification: a contiguous partial cache
+ *   spec_verify_mode        built from a budget list, and the full / partial
+ *                           schedule.
  *
  * Conventions for every call
  *   - Tensor arguments are DEVICE pointers owned by the caller.  The library
@@ -81,6 +84,9 @@ enum {
   SPEC_E_HIP = -4,           /* the HIP runtime reported an error */
   SPEC_E_DEVICE_RANGE = -5   /* a kernel found an out-of-range device value */
 };
+
+/* Verification schedule (spec_verify_mode). */
+enum { SPEC_VERIFY_FULL = 0, SPEC_VERIFY_PARTIAL = 1 };
 
 /* Element types of q, K, V and out. */
 enum { SPEC_F32 = 0, SPEC_BF16 = 1 };
@@ -296,8 +302,11 @@ spec_status spec_block_means(const spec_dims* dims, const spec_kv* cache, const 
  *   - idx[b][h][0..budget) receives the listed positions whose pad byte is 0,
  *     in increasing order, then -1 entries up to the budget: the list is the
  *     budget-mode input of spec_attn_draft_sparse (idx_stride_h = budget).
- * scores_or_null[b][h][0..max_blocks) receives the block scores, NaN for
- * blocks that are not candidates or have no score.  q is [B][Tq][Hq][D]
+ * With shared != 0 there is one list per sequence, idx[b][0][0..budget): a
+ * block's score is the mean of its Hkv heads' scores, as a partial cache
+ * keeps whole cache-manager blocks (spec_kv_gather takes such lists).
+ * scores_or_null[b][h or 0][0..max_blocks) receives the block scores, NaN
+ * for blocks that are not candidates or have no score.  q is [B][Tq][Hq][D]
  * (dims->dtype), means as written by spec_block_means for every block below
  * capacity (max_blocks * block >= capacity; max_blocks <= 8192).
  * Requirements: budget >= n_sink + window + n_select * block, n_select <=
@@ -309,9 +318,53 @@ spec_status spec_select_blocks(const spec_dims* dims, const void* q, int32_t n_q
                                const float* means, int32_t max_blocks, int32_t block,
                                const int32_t* cache_len, int32_t capacity,
                                const uint8_t* pad_or_null, int64_t pad_stride_b, int32_t n_sink,
-                               int32_t window, int32_t n_select, int32_t* idx, int32_t budget,
-                               float* scores_or_null, void* workspace, size_t workspace_bytes,
-                               void* stream);
+                               int32_t window, int32_t n_select, int32_t shared, int32_t* idx,
+                               int32_t budget, float* scores_or_null, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/*
+ * Partial KV cache for partial verification ([PV] section 3.2: a sink,
+ * retrieved blocks, a local window and a buffer, contiguous in token order
+ * and handled as one KV segment; section 3.3: a full verification refreshes
+ * it).
+ *
+ * idx holds one budget list per sequence, idx[b * idx_stride_b + j] for j <
+ * budget (e.g. spec_select_blocks with shared != 0).  Slot j of every KV head
+ * of `partial` receives the K and V rows of position idx[b][j]; a -1 entry
+ * gives a padding slot (zero K/V, partial_pad[b][j] = 1), a listed position
+ * gives partial_pad[b][j] = 0, and partial_len[b] = budget.  Slots at or past
+ * the budget are not touched: the buffer of later tokens goes there through
+ * spec_kv_commit on the partial cache.  Partial verification is then
+ * spec_attn_verify_tree over (partial, partial_len, partial_pad); the
+ * pos_ids it returns count the partial cache's valid slots, so a caller that
+ * needs the full sequence's positions takes them from its last full
+ * verification plus the tokens committed since.
+ *
+ * A listed value outside [0, cache_len[b]) other than -1 raises
+ * SPEC_DEV_INDEX and gives a padding slot; cache_len[b] outside
+ * [0, capacity] raises SPEC_DEV_CACHE_LEN and pads every slot.  partial
+ * follows the spec_kv layout rules with capacity >= budget; partial_pad is
+ * uint8 [B][partial_pad_stride_b], stride >= partial capacity.  batch at
+ * most 65535.  Workspace: spec_select_workspace_bytes(dims, 0) bytes.
+ */
+spec_status spec_kv_gather(int32_t batch, int32_t n_kv_heads, int32_t head_dim, int32_t dtype,
+                           const spec_kv* cache, const int32_t* cache_len, const int32_t* idx,
+                           int32_t budget, int64_t idx_stride_b, const spec_kv_mut* partial,
+                           int32_t* partial_len, uint8_t* partial_pad,
+                           int64_t partial_pad_stride_b, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/*
+ * Full or partial verification for the next step ([PV] section 3.3), a host
+ * computation: SPEC_VERIFY_FULL while the sequence (seq_len tokens) is
+ * shorter than the partial budget, or when the partially verified tokens
+ * kept in the buffer plus the n_nodes new candidates exceed
+ * buffer_capacity; SPEC_VERIFY_PARTIAL otherwise.  A full verification
+ * refreshes the partial cache and empties the buffer.  Negative arguments,
+ * budget < 1 or n_nodes < 1 return SPEC_E_INVALID.
+ */
+int32_t spec_verify_mode(int64_t seq_len, int32_t budget, int32_t buffered, int32_t n_nodes,
+                         int32_t buffer_capacity);
 
 /* Workspace sizes in bytes (0 on invalid arguments; see spec_last_error).
  * max_view_len for the draft: min(capacity, n_sink + window + n_q_tokens - 1)

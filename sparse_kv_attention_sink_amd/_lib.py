@@ -30,12 +30,14 @@ SPEC_DEV_INDEX = 2
 SPEC_DEV_PARENT = 4
 SPEC_DEV_DEPTH = 8
 SPEC_DEV_COMMIT = 16
+SPEC_VERIFY_FULL = 0
+SPEC_VERIFY_PARTIAL = 1
 
 EXPORTED = [
     "spec_attn_draft_sparse", "spec_attn_verify_tree", "spec_accept_greedy", "spec_kv_commit",
     "spec_draft_workspace_bytes", "spec_verify_workspace_bytes", "spec_accept_workspace_bytes",
     "spec_commit_workspace_bytes", "spec_block_means", "spec_select_blocks",
-    "spec_select_workspace_bytes",
+    "spec_select_workspace_bytes", "spec_kv_gather", "spec_verify_mode",
     "spec_device_status", "spec_status_string", "spec_last_error", "spec_abi_version",
 ]
 
@@ -83,10 +85,14 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.spec_commit_workspace_bytes.restype = SZ
     lib.spec_block_means.argtypes = [P, P, P, P, I64, I32, I32, I32, P, I32, P, SZ, P]
     lib.spec_block_means.restype = I32
-    lib.spec_select_blocks.argtypes = [P, P, I32, P, I32, I32, P, I32, P, I64, I32, I32, I32, P,
-                                       I32, P, P, SZ, P]
+    lib.spec_select_blocks.argtypes = [P, P, I32, P, I32, I32, P, I32, P, I64, I32, I32, I32, I32,
+                                       P, I32, P, P, SZ, P]
     lib.spec_select_blocks.restype = I32
     lib.spec_select_workspace_bytes.argtypes = [P, I32]
+    lib.spec_kv_gather.argtypes = [I32, I32, I32, I32, P, P, P, I32, I64, P, P, P, I64, P, SZ, P]
+    lib.spec_kv_gather.restype = I32
+    lib.spec_verify_mode.argtypes = [I64, I32, I32, I32, I32]
+    lib.spec_verify_mode.restype = I32
     lib.spec_select_workspace_bytes.restype = SZ
     lib.spec_draft_workspace_bytes.argtypes = [P, I32, I32]
     lib.spec_draft_workspace_bytes.restype = SZ
@@ -370,9 +376,11 @@ def spec_block_means(k_cache, cache_len, block, *, pad=None, first_block=0, n_bl
 
 
 def spec_select_blocks(q, means, cache_len, *, block, capacity, n_sink, window, n_select, budget,
-                       pad=None, idx=None, scores=None, want_scores=False, workspace=None):
-    """Budget lists ``[B, Hkv, budget]`` int32 (sink, best-scoring blocks,
-    window; -1 padded) from block means.  Returns (idx, scores or None)."""
+                       pad=None, shared=False, idx=None, scores=None, want_scores=False,
+                       workspace=None):
+    """Budget lists ``[B, Hkv, budget]`` (``[B, 1, budget]`` when shared)
+    int32 (sink, best-scoring blocks, window; -1 padded) from block means.
+    Returns (idx, scores or None)."""
     lib = load()
     _on_gpu(q, means, cache_len, pad, idx, scores)
     if q.dim() != 4 or not q.is_contiguous():
@@ -385,19 +393,67 @@ def spec_select_blocks(q, means, cache_len, *, block, capacity, n_sink, window, 
     if cache_len.dtype != torch.int32 or cache_len.numel() != B or not cache_len.is_contiguous():
         raise ValueError("cache_len must be a contiguous int32 [B] tensor")
     pad_t, psb = _pad_arg(pad, B, capacity)
+    n_lists = 1 if shared else Hkv
     if idx is None:
-        idx = torch.empty((B, Hkv, budget), dtype=torch.int32, device=q.device)
+        idx = torch.empty((B, n_lists, budget), dtype=torch.int32, device=q.device)
     if scores is None and want_scores:
-        scores = torch.empty((B, Hkv, max_blocks), dtype=torch.float32, device=q.device)
+        scores = torch.empty((B, n_lists, max_blocks), dtype=torch.float32, device=q.device)
+    if tuple(idx.shape) != (B, n_lists, budget) or idx.dtype != torch.int32 or not idx.is_contiguous():
+        raise ValueError("idx must be a contiguous int32 [B, 1 or Hkv, budget] tensor")
     dims = make_dims(B, Hq, Hkv, D, _dtype_code(q))
     if workspace is None:
         workspace = new_workspace(select_workspace_bytes(dims, max_blocks), q.device)
     st = lib.spec_select_blocks(ctypes.byref(dims), _ptr(q), T, _ptr(means), max_blocks, block,
                                 _ptr(cache_len), capacity, _ptr(pad_t), psb, n_sink, window,
-                                n_select, _ptr(idx), budget, _ptr(scores), _ptr(workspace),
-                                workspace.numel(), _stream(q))
+                                n_select, int(bool(shared)), _ptr(idx), budget, _ptr(scores),
+                                _ptr(workspace), workspace.numel(), _stream(q))
     _check(st)
     return idx, scores
+
+
+def spec_kv_gather(k_cache, v_cache, cache_len, idx, *, partial_k=None, partial_v=None,
+                   partial_len=None, partial_pad=None, capacity=None, workspace=None):
+    """Build the partial cache from one budget list per sequence (``idx``
+    int32 ``[B, 1, budget]`` or ``[B, budget]``).  Returns (partial_k,
+    partial_v, partial_len, partial_pad); the partial tensors are allocated
+    (zero-filled) with ``capacity`` slots (default: the budget) when None."""
+    lib = load()
+    _on_gpu(k_cache, v_cache, cache_len, idx, partial_k, partial_v, partial_len, partial_pad)
+    B, Hkv, _, D = k_cache.shape
+    if idx.dtype != torch.int32 or idx.shape[0] != B or idx.stride(-1) != 1 or \
+            (idx.dim() == 3 and idx.shape[1] != 1) or idx.dim() not in (2, 3):
+        raise ValueError("idx must be int32 [B, 1, budget] or [B, budget]")
+    budget = idx.shape[-1]
+    if cache_len.dtype != torch.int32 or cache_len.numel() != B or not cache_len.is_contiguous():
+        raise ValueError("cache_len must be a contiguous int32 [B] tensor")
+    dev = k_cache.device
+    cap = budget if capacity is None else capacity
+    if partial_k is None:
+        partial_k = torch.zeros((B, Hkv, cap, D), dtype=k_cache.dtype, device=dev)
+        partial_v = torch.zeros_like(partial_k)
+    if partial_len is None:
+        partial_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if partial_pad is None:
+        partial_pad = torch.zeros((B, (partial_k.shape[2] + 3) // 4 * 4), dtype=torch.uint8, device=dev)
+    kv = _kv(k_cache, v_cache)
+    pkv = _kv(partial_k, partial_v)
+    if workspace is None:
+        workspace = new_workspace(256, dev)
+    st = lib.spec_kv_gather(B, Hkv, D, _dtype_code(k_cache), ctypes.byref(kv), _ptr(cache_len),
+                            _ptr(idx), budget, idx.stride(0), ctypes.byref(pkv), _ptr(partial_len),
+                            _ptr(partial_pad), partial_pad.stride(0), _ptr(workspace),
+                            workspace.numel(), _stream(k_cache))
+    _check(st)
+    return partial_k, partial_v, partial_len, partial_pad
+
+
+def spec_verify_mode(seq_len: int, budget: int, buffered: int, n_nodes: int,
+                     buffer_capacity: int) -> int:
+    """SPEC_VERIFY_FULL or SPEC_VERIFY_PARTIAL for the next step (host only)."""
+    r = load().spec_verify_mode(seq_len, budget, buffered, n_nodes, buffer_capacity)
+    if r < 0:
+        _check(r)
+    return int(r)
 
 
 def spec_device_status(workspace: torch.Tensor) -> int:

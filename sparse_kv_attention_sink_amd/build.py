@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libspecattn.so")
-SOURCES = ["api.hip", "attn.hip", "generic.hip", "accept.hip", "commit.hip", "select.hip"]
+SOURCES = ["api.hip", "attn.hip", "generic.hip", "accept.hip", "commit.hip", "select.hip", "gather.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

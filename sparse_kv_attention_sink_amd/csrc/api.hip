@@ -613,9 +613,9 @@ spec_status spec_select_blocks(const spec_dims* dims, const void* q, int32_t n_q
                                const float* means, int32_t max_blocks, int32_t block,
                                const int32_t* cache_len, int32_t capacity,
                                const uint8_t* pad_or_null, int64_t pad_stride_b, int32_t n_sink,
-                               int32_t window, int32_t n_select, int32_t* idx, int32_t budget,
-                               float* scores_or_null, void* workspace, size_t workspace_bytes,
-                               void* stream) {
+                               int32_t window, int32_t n_select, int32_t shared, int32_t* idx,
+                               int32_t budget, float* scores_or_null, void* workspace,
+                               size_t workspace_bytes, void* stream) {
   spec_status st = check_dims(dims);
   if (st != SPEC_OK) return st;
   if (n_q_tokens < 1) return fail(SPEC_E_INVALID, "n_q_tokens %d < 1", n_q_tokens);
@@ -663,6 +663,7 @@ spec_status spec_select_blocks(const spec_dims* dims, const void* q, int32_t n_q
   a.window = window;
   a.n_select = n_select;
   a.budget = budget;
+  a.shared = shared != 0;
   a.cache_len = cache_len;
   a.pad = pad_or_null;
   a.pad_sb = pad_stride_b;
@@ -673,6 +674,78 @@ spec_status spec_select_blocks(const spec_dims* dims, const void* q, int32_t n_q
   hipError_t e = launch_select_blocks(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "block selection launch");
   return SPEC_OK;
+}
+
+spec_status spec_kv_gather(int32_t batch, int32_t n_kv_heads, int32_t head_dim, int32_t dtype,
+                           const spec_kv* cache, const int32_t* cache_len, const int32_t* idx,
+                           int32_t budget, int64_t idx_stride_b, const spec_kv_mut* partial,
+                           int32_t* partial_len, uint8_t* partial_pad,
+                           int64_t partial_pad_stride_b, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  const spec_dims d{batch, n_kv_heads, n_kv_heads, head_dim, dtype, 1.f};
+  spec_status st = check_dims(&d);
+  if (st != SPEC_OK) return st;
+  if (budget < 1) return fail(SPEC_E_INVALID, "budget %d < 1", budget);
+  if (batch > 65535) return fail(SPEC_E_UNSUPPORTED, "batch must be <= 65535");
+  if (batch == 0) return SPEC_OK;
+  if ((st = check_kv(cache, &d, "cache", true)) != SPEC_OK) return st;
+  if (partial == nullptr) return fail(SPEC_E_INVALID, "partial is NULL");
+  const spec_kv pc{partial->k, partial->v, partial->stride_b, partial->stride_h, partial->stride_t,
+                   partial->capacity};
+  if ((st = check_kv(&pc, &d, "partial", true)) != SPEC_OK) return st;
+  if (partial->capacity < budget)
+    return fail(SPEC_E_INVALID, "partial capacity %d < budget %d", partial->capacity, budget);
+  if (cache_len == nullptr || idx == nullptr || partial_len == nullptr || partial_pad == nullptr)
+    return fail(SPEC_E_INVALID, "a required pointer is NULL");
+  if (!aligned(cache_len, 4) || !aligned(idx, 4) || !aligned(partial_len, 4))
+    return fail(SPEC_E_INVALID, "int32 arrays must be 4-byte aligned");
+  if (idx_stride_b < budget) return fail(SPEC_E_INVALID, "idx_stride_b %lld < budget %d",
+                                         (long long)idx_stride_b, budget);
+  if (partial_pad_stride_b < partial->capacity)
+    return fail(SPEC_E_INVALID, "partial_pad_stride_b %lld < partial capacity %d",
+                (long long)partial_pad_stride_b, partial->capacity);
+  if (workspace == nullptr || workspace_bytes < kHeaderBytes)
+    return fail(SPEC_E_WORKSPACE, "workspace of %zu bytes needed", kHeaderBytes);
+  if (!aligned(workspace, 256)) return fail(SPEC_E_INVALID, "workspace must be 256-byte aligned");
+  const int64_t es = esize(dtype);
+  GatherArgs a;
+  a.k = static_cast<const char*>(cache->k);
+  a.v = static_cast<const char*>(cache->v);
+  a.c_sb = cache->stride_b * es;
+  a.c_sh = cache->stride_h * es;
+  a.c_st = cache->stride_t * es;
+  a.pk = static_cast<char*>(partial->k);
+  a.pv = static_cast<char*>(partial->v);
+  a.p_sb = partial->stride_b * es;
+  a.p_sh = partial->stride_h * es;
+  a.p_st = partial->stride_t * es;
+  a.batch = batch;
+  a.n_kv_heads = n_kv_heads;
+  a.row_chunks = (int32_t)(head_dim * es / 16);
+  a.budget = budget;
+  a.capacity = cache->capacity;
+  a.cache_len = cache_len;
+  a.idx = idx;
+  a.idx_sb = idx_stride_b;
+  a.partial_len = partial_len;
+  a.partial_pad = partial_pad;
+  a.pad_sb = partial_pad_stride_b;
+  a.err = static_cast<uint32_t*>(workspace);
+  hipError_t e = launch_kv_gather(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "kv gather launch");
+  return SPEC_OK;
+}
+
+int32_t spec_verify_mode(int64_t seq_len, int32_t budget, int32_t buffered, int32_t n_nodes,
+                         int32_t buffer_capacity) {
+  if (seq_len < 0 || budget < 1 || buffered < 0 || n_nodes < 1 || buffer_capacity < 0) {
+    fail(SPEC_E_INVALID, "need seq_len >= 0, budget >= 1, buffered >= 0, n_nodes >= 1, "
+                         "buffer_capacity >= 0");
+    return SPEC_E_INVALID;
+  }
+  if (seq_len < budget) return SPEC_VERIFY_FULL;
+  if ((int64_t)buffered + n_nodes > buffer_capacity) return SPEC_VERIFY_FULL;
+  return SPEC_VERIFY_PARTIAL;
 }
 
 size_t spec_select_workspace_bytes(const spec_dims* dims, int32_t max_blocks) {

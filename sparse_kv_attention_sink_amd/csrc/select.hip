@@ -197,9 +197,11 @@ __global__ __launch_bounds__(256) void select_blocks_kernel(SelectArgs a) {
   __shared__ int sel_s[kMaxSelect];
   __shared__ int segcnt_s[kMaxSelect + 2];
 
-  int32_t* out = a.idx + ((int64_t)b * a.n_kv_heads + g) * a.budget;
+  // one list per (sequence, KV head), or per sequence when shared (g = 0)
+  const int n_lists = a.shared ? 1 : a.n_kv_heads;
+  int32_t* out = a.idx + ((int64_t)b * n_lists + g) * a.budget;
   float* sc_out = a.scores == nullptr ? nullptr
-                                      : a.scores + ((int64_t)b * a.n_kv_heads + g) * a.max_blocks;
+                                      : a.scores + ((int64_t)b * n_lists + g) * a.max_blocks;
   const int L0 = a.cache_len[b];
   if (L0 < 0 || L0 > a.capacity) {
     if (tid == 0 && g == 0) raise_error(a.err, SPEC_DEV_CACHE_LEN);
@@ -215,9 +217,16 @@ __global__ __launch_bounds__(256) void select_blocks_kernel(SelectArgs a) {
   int c_lo, nc;
   candidate_range(a, L, &c_lo, &nc);
   const float* sw = a.sc_ws + ((int64_t)b * a.n_kv_heads + g) * a.max_blocks;
-  for (int i = tid; i < nc; i += 256) key_s[i] = score_key(sw[c_lo + i]);
+  const int64_t hs = a.max_blocks;   // head stride of the workspace scores
+  auto score_of = [&](int c) -> float {
+    if (!a.shared) return sw[c];
+    float t = 0.f;
+    for (int h = 0; h < a.n_kv_heads; ++h) t += sw[h * hs + c];
+    return t / (float)a.n_kv_heads;
+  };
+  for (int i = tid; i < nc; i += 256) key_s[i] = score_key(score_of(c_lo + i));
   if (sc_out != nullptr)
-    for (int c = tid; c < a.max_blocks; c += 256) sc_out[c] = sw[c];
+    for (int c = tid; c < a.max_blocks; c += 256) sc_out[c] = score_of(c);
   __syncthreads();
 
   // how many blocks have a score, and how many are chosen
@@ -382,8 +391,9 @@ hipError_t launch_select_blocks(const SelectArgs& a, hipStream_t st) {
                      dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(select_blocks_kernel, dim3((unsigned)a.n_kv_heads, (unsigned)a.batch),
-                     dim3(256), 0, st, a);
+  hipLaunchKernelGGL(select_blocks_kernel,
+                     dim3(a.shared ? 1u : (unsigned)a.n_kv_heads, (unsigned)a.batch), dim3(256), 0,
+                     st, a);
   return hipGetLastError();
 }
 

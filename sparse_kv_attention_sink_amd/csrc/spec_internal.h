@@ -132,13 +132,31 @@ struct SelectArgs {
   const void* q;                       // [B][T][Hq][D]
   int32_t bf16, T, Hq, G, head_dim, batch, n_kv_heads, capacity;
   const float* means;                  // [B][Hkv][max_blocks][D]
-  int32_t max_blocks, block, n_sink, window, n_select, budget;
+  int32_t max_blocks, block, n_sink, window, n_select, budget, shared;
   const int32_t* cache_len;
   const uint8_t* pad;
   int64_t pad_sb;
   int32_t* idx;                        // [B][Hkv][budget]
   float* scores;                       // [B][Hkv][max_blocks] or null
   float* sc_ws;                        // [B][Hkv][max_blocks] workspace scores
+  uint32_t* err;
+};
+
+// Arguments of the partial-cache gather kernel (byte strides).
+struct GatherArgs {
+  const char* k;
+  const char* v;
+  int64_t c_sb, c_sh, c_st;
+  char* pk;
+  char* pv;
+  int64_t p_sb, p_sh, p_st;
+  int32_t batch, n_kv_heads, row_chunks, budget, capacity;
+  const int32_t* cache_len;
+  const int32_t* idx;                  // [B][budget] (one list per sequence)
+  int64_t idx_sb;
+  int32_t* partial_len;
+  uint8_t* partial_pad;
+  int64_t pad_sb;
   uint32_t* err;
 };
 
@@ -157,5 +175,6 @@ hipError_t launch_accept(int B, int N, int V, const float* logits, const int32_t
 hipError_t launch_kv_commit(const CommitArgs& a, hipStream_t st);
 hipError_t launch_block_means(const MeansArgs& a, hipStream_t st);
 hipError_t launch_select_blocks(const SelectArgs& a, hipStream_t st);
+hipError_t launch_kv_gather(const GatherArgs& a, hipStream_t st);
 
 }  // namespace spec

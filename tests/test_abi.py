@@ -219,10 +219,11 @@ def test_block_means_rejects_bad_arguments(lib, bad, status):
 
 
 def select_call(lib, d, *, q=FAKE, tq=1, means=FAKE, max_blocks=256, block=16, cl=FAKE, cap=4096,
-                pad=None, pad_sb=0, sink=4, win=64, nsel=8, idx=FAKE, budget=196, scores=None,
-                ws=FAKE, wsb=1 << 30):
+                pad=None, pad_sb=0, sink=4, win=64, nsel=8, shared=0, idx=FAKE, budget=196,
+                scores=None, ws=FAKE, wsb=1 << 30):
     return lib.spec_select_blocks(ctypes.byref(d), q, tq, means, max_blocks, block, cl, cap, pad,
-                                  pad_sb, sink, win, nsel, idx, budget, scores, ws, wsb, None)
+                                  pad_sb, sink, win, nsel, shared, idx, budget, scores, ws, wsb,
+                                  None)
 
 
 @pytest.mark.parametrize("bad,status", [
@@ -245,6 +246,46 @@ def test_select_blocks_rejects_bad_arguments(lib, bad, status):
     assert select_call(lib, dims(), **bad) == status
 
 
+def gather_call(lib, *, B=2, hkv=8, D=128, dtype=skg.SPEC_BF16, cache=None, cl=FAKE, idx=FAKE,
+                budget=64, isb=64, partial=None, plen=FAKE, ppad=FAKE, ppsb=64, ws=FAKE, wsb=256):
+    cache = cache or kv()
+    partial = partial or kv(cap=64)
+    return lib.spec_kv_gather(B, hkv, D, dtype, ctypes.byref(cache), cl, idx, budget, isb,
+                              ctypes.byref(partial), plen, ppad, ppsb, ws, wsb, None)
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(budget=0), skg.SPEC_E_INVALID),
+    (dict(B=-1), skg.SPEC_E_INVALID),
+    (dict(D=96), skg.SPEC_E_UNSUPPORTED),
+    (dict(budget=65, isb=65), skg.SPEC_E_INVALID),           # partial capacity 64 < budget
+    (dict(isb=63), skg.SPEC_E_INVALID),
+    (dict(idx=None), skg.SPEC_E_INVALID),
+    (dict(idx=FAKE + 2), skg.SPEC_E_INVALID),
+    (dict(plen=None), skg.SPEC_E_INVALID),
+    (dict(ppad=None), skg.SPEC_E_INVALID),
+    (dict(ppsb=63), skg.SPEC_E_INVALID),
+    (dict(partial=kv(cap=64, ptr=FAKE + 8)), skg.SPEC_E_INVALID),
+    (dict(cache=kv(stride_t=64)), skg.SPEC_E_INVALID),
+    (dict(wsb=8), skg.SPEC_E_WORKSPACE),
+])
+def test_gather_rejects_bad_arguments(lib, bad, status):
+    assert gather_call(lib, **bad) == status
+
+
+def test_verify_mode_follows_the_schedule_table(lib):
+    """The host-side schedule against the hand-enumerated table of SpecPV
+    section 3.3 (the same fixture pins the oracle)."""
+    import json
+    with open(os.path.join(ROOT, "tests", "golden", "verify_mode_specpv.json")) as f:
+        fx = json.load(f)
+    for case in fx["cases"]:
+        *args, mode = case
+        assert lib.spec_verify_mode(*args) == mode, case
+    assert lib.spec_verify_mode(-1, 4096, 0, 3, 64) == skg.SPEC_E_INVALID
+    assert lib.spec_verify_mode(100, 4096, 0, 0, 64) == skg.SPEC_E_INVALID
+
+
 def test_device_status_rejects_null(lib):
     assert lib.spec_device_status(None, None, None) == skg.SPEC_E_INVALID
 
@@ -258,6 +299,7 @@ def test_empty_batch_is_a_no_op(lib):
     assert commit(lib, B=0) == skg.SPEC_OK
     assert means_call(lib, dims(B=0)) == skg.SPEC_OK
     assert select_call(lib, dims(B=0)) == skg.SPEC_OK
+    assert gather_call(lib, B=0) == skg.SPEC_OK
     d = dims(B=8)
     assert lib.spec_select_workspace_bytes(ctypes.byref(d), 0) == 256
     assert lib.spec_select_workspace_bytes(ctypes.byref(d), 1024) == 256 + 8 * 8 * 1024 * 4
