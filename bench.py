@@ -355,6 +355,87 @@ def run_commit(torch, skg, *, B, L, widths, depths, seed, reps=60):
                 gbs=round(moved / (us * 1e-6) / 1e9, 1))
 
 
+# ------------------------------------------------------------ partial verification
+
+def run_partial_1m(torch, skg, layers, *, block=128, budget=4096, buffer=64, window=2048,
+                   reps=3):
+    """Partial verification at the 1M layer: per layer a block-mean table
+    (blocks of 128), a shared selection (sink 4, window 2048, the rest in
+    blocks), a partial cache of `budget` slots plus a buffer; then the
+    chain-3 verify over each layer's partial cache, timed as a pass over the
+    32 layers (as the step runs them), against the full-cache verify."""
+    dev = torch.device("cuda:0")
+    cl = torch.tensor([L1M], dtype=torch.int32, device=dev)
+    parents = torch.tensor([-1, 0, 1], dtype=torch.int32, device=dev)
+    n_select = (budget - 4 - window) // block
+    nb = L1M // block
+    dims = skg.make_dims(1, HQ, HKV, D, skg.SPEC_BF16)
+    ws_s = skg.new_workspace(skg.select_workspace_bytes(dims, nb), dev)
+    ws_v = skg.new_workspace(skg.verify_workspace_bytes(dims, CHAIN, budget + buffer), dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    # outputs allocated up front, so that the timed passes run kernels only
+    means = torch.empty((1, HKV, nb, D), dtype=torch.float32, device=dev)
+    idxs = [torch.empty((1, 1, budget), dtype=torch.int32, device=dev) for _ in layers]
+    parts = []
+    for _ in layers:
+        pk = torch.zeros((1, HKV, budget + buffer, D), dtype=torch.bfloat16, device=dev)
+        parts.append((pk, torch.zeros_like(pk), torch.empty(1, dtype=torch.int32, device=dev),
+                      torch.zeros((1, budget + buffer), dtype=torch.uint8, device=dev)))
+
+    def refresh(phase):
+        for lay, idx, (pk, pv, plen, ppad) in zip(layers, idxs, parts):
+            if phase in ("means", "all"):
+                skg.spec_block_means(lay["k"], cl, block, means=means, workspace=ws_s)
+            if phase in ("select", "all"):
+                skg.spec_select_blocks(lay["verify_q"], means, cl, block=block, capacity=L1M,
+                                       n_sink=4, window=window, n_select=n_select, budget=budget,
+                                       shared=True, idx=idx, workspace=ws_s)
+            if phase in ("gather", "all"):
+                skg.spec_kv_gather(lay["k"], lay["v"], cl, idx, partial_k=pk, partial_v=pv,
+                                   partial_len=plen, partial_pad=ppad, workspace=ws_s)
+    refresh("all")
+    torch.cuda.synchronize()
+    t_phase = {}
+    for phase in ("means", "select", "gather"):
+        a, b = ev(), ev()
+        prerecord([a, b], torch)
+        torch.cuda._sleep(int(3e7))      # the host queues the whole pass first
+        a.record()
+        refresh(phase)
+        b.record()
+        torch.cuda.synchronize()
+        t_phase[phase] = a.elapsed_time(b) / len(layers) * 1e3
+    assert skg.spec_device_status(ws_s) == 0
+    out = torch.empty((1, CHAIN, HQ, D), dtype=torch.bfloat16, device=dev)
+
+    def pass_(pad=True):
+        for lay, (pk, pv, plen, ppad) in zip(layers, parts):
+            skg.spec_attn_verify_tree(lay["verify_q"], pk, pv, plen, lay["tree_k"], lay["tree_v"],
+                                      parents, pad=ppad, out=out, want_lse=False,
+                                      want_pos_ids=False, workspace=ws_v)
+    pass_()
+    torch.cuda.synchronize()
+    a, b = ev(), ev()
+    prerecord([a, b], torch)
+    a.record()
+    for _ in range(reps):
+        pass_()
+    b.record()
+    torch.cuda.synchronize()
+    assert skg.spec_device_status(ws_v) == 0
+    per_layer_us = a.elapsed_time(b) / (reps * len(layers)) * 1e3
+    part_bytes = HKV * (budget + buffer) * 2 * D * 2 + (budget + buffer)
+    del parts, idxs, means
+    torch.cuda.empty_cache()
+    return dict(block=block, budget=budget, buffer=buffer, window=window, n_select=n_select,
+                verify_partial_us_per_layer=round(per_layer_us, 2),
+                verify_partial_gbs=round(part_bytes / (per_layer_us * 1e-6) / 1e9, 1),
+                refresh_us_per_layer={k: round(v, 2) for k, v in t_phase.items()},
+                refresh_note="per layer, at a full verification: the whole mean table (in a "
+                             "decode loop only the blocks an append changed), the selection and "
+                             "the gather of the partial cache")
+
+
 # ------------------------------------------------------------ budget selection
 
 def run_select(torch, skg, *, B=8, L=16384, block=16, reps=24, seed=8400):
@@ -561,6 +642,10 @@ def main():
     if not args.skip_cpu:
         cpu = cpu_baseline(layers, torch)
         log(f"[bench] cpu oracle: {cpu['value']:.3f} GB/s")
+    partial = run_partial_1m(torch, skg, layers)
+    partial["verify_full_us_per_layer"] = round(r1m["verify_avg_ms"] * 1e3, 2)
+    log(f"[bench] partial verify: {partial['verify_partial_us_per_layer']} us per layer "
+        f"(full {partial['verify_full_us_per_layer']} us)")
     del layers
     torch.cuda.empty_cache()
     r16 = None if args.skip_16k else run_16k(args, torch, skg)
@@ -609,6 +694,7 @@ def main():
         "ctx16k": r16,
         "kv_commit": commit,
         "budget_select": select,
+        "partial_verify_1m": partial,
     }
     print(json.dumps(line), flush=True)
 

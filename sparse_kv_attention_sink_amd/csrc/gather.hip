@@ -19,7 +19,8 @@ namespace spec {
 
 namespace {
 
-constexpr int kGatherSlots = 32;
+constexpr int kGatherSlots = 8;
+constexpr int kGatherUnroll = 8;   // chunks a thread loads before it stores them
 
 __global__ __launch_bounds__(256) void kv_gather_kernel(GatherArgs a) {
   const int b = blockIdx.y, tid = threadIdx.x;
@@ -46,17 +47,31 @@ __global__ __launch_bounds__(256) void kv_gather_kernel(GatherArgs a) {
   const int CH = a.row_chunks;
   const int per_slot = a.n_kv_heads * CH;              // chunks of one slot (K or V)
   const int n = min(kGatherSlots, a.budget - j0) * per_slot;
-  for (int w = tid; w < 2 * n; w += 256) {
-    const int which = w >= n;                          // 0: K, 1: V
-    const int r = which ? w - n : w;
-    const int jj = r / per_slot, h = (r / CH) % a.n_kv_heads, ch = r % CH;
-    const int p = pos_s[jj];
-    u32x4 val = u32x4{0, 0, 0, 0};
-    if (p >= 0)
-      val = *reinterpret_cast<const u32x4*>((which ? a.v : a.k) + (int64_t)b * a.c_sb +
-                                            (int64_t)h * a.c_sh + (int64_t)p * a.c_st + ch * 16);
-    *reinterpret_cast<u32x4*>((which ? a.pv : a.pk) + (int64_t)b * a.p_sb + (int64_t)h * a.p_sh +
-                              (int64_t)(j0 + jj) * a.p_st + ch * 16) = val;
+  // every thread loads its chunks of a round first, then stores them
+  for (int w0 = 0; w0 < 2 * n; w0 += 256 * kGatherUnroll) {
+    u32x4 val[kGatherUnroll];
+    char* dst[kGatherUnroll];
+#pragma unroll
+    for (int u = 0; u < kGatherUnroll; ++u) {
+      const int w = w0 + u * 256 + tid;
+      val[u] = u32x4{0, 0, 0, 0};
+      dst[u] = nullptr;
+      if (w < 2 * n) {
+        const int which = w >= n;                      // 0: K, 1: V
+        const int r = which ? w - n : w;
+        const int jj = r / per_slot, h = (r / CH) % a.n_kv_heads, ch = r % CH;
+        const int p = pos_s[jj];
+        if (p >= 0)
+          val[u] = *reinterpret_cast<const u32x4*>((which ? a.v : a.k) + (int64_t)b * a.c_sb +
+                                                   (int64_t)h * a.c_sh + (int64_t)p * a.c_st +
+                                                   ch * 16);
+        dst[u] = (which ? a.pv : a.pk) + (int64_t)b * a.p_sb + (int64_t)h * a.p_sh +
+                 (int64_t)(j0 + jj) * a.p_st + ch * 16;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kGatherUnroll; ++u)
+      if (dst[u] != nullptr) *reinterpret_cast<u32x4*>(dst[u]) = val[u];
   }
 }
 

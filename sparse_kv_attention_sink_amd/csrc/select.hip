@@ -30,6 +30,7 @@ namespace {
 
 constexpr int kMeanBlocksPerWG = 4;   // one block per wavefront
 constexpr int kScoreSteps = 8;
+constexpr int kWindowSegs = 64;      // pieces the window is listed in
 constexpr int kScoreBlocksPerWG = 16 * kScoreSteps;   // 4 wavefronts x 4 blocks x steps
 
 __global__ __launch_bounds__(256) void block_means_kernel(MeansArgs a) {
@@ -195,7 +196,7 @@ __global__ __launch_bounds__(256) void select_blocks_kernel(SelectArgs a) {
   __shared__ int red4[4];
   __shared__ int s_digit, s_above;
   __shared__ int sel_s[kMaxSelect];
-  __shared__ int segcnt_s[kMaxSelect + 2];
+  __shared__ int segcnt_s[kMaxSelect + 1 + kWindowSegs];
 
   // one list per (sequence, KV head), or per sequence when shared (g = 0)
   const int n_lists = a.shared ? 1 : a.n_kv_heads;
@@ -218,15 +219,51 @@ __global__ __launch_bounds__(256) void select_blocks_kernel(SelectArgs a) {
   candidate_range(a, L, &c_lo, &nc);
   const float* sw = a.sc_ws + ((int64_t)b * a.n_kv_heads + g) * a.max_blocks;
   const int64_t hs = a.max_blocks;   // head stride of the workspace scores
-  auto score_of = [&](int c) -> float {
-    if (!a.shared) return sw[c];
-    float t = 0.f;
-    for (int h = 0; h < a.n_kv_heads; ++h) t += sw[h * hs + c];
-    return t / (float)a.n_kv_heads;
+  // scores of blocks c0 + u * 256 (u < 4) for this thread: the KV head's own,
+  // or (shared) the mean over the heads, summed in head order with up to
+  // 8 heads x 4 blocks of loads in flight
+  auto scores4 = [&](int c0, int c_end, float (&t)[4]) {
+    if (!a.shared) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) t[u] = c0 + u * 256 < c_end ? sw[c0 + u * 256] : 0.f;
+      return;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) t[u] = 0.f;
+    for (int h0 = 0; h0 < a.n_kv_heads; h0 += 8) {
+      float x[8][4];
+#pragma unroll
+      for (int hh = 0; hh < 8; ++hh)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int c = c0 + u * 256;
+          x[hh][u] = (h0 + hh < a.n_kv_heads && c < c_end) ? sw[(h0 + hh) * hs + c] : 0.f;
+        }
+#pragma unroll
+      for (int hh = 0; hh < 8; ++hh)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (h0 + hh < a.n_kv_heads) t[u] += x[hh][u];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) t[u] /= (float)a.n_kv_heads;
   };
-  for (int i = tid; i < nc; i += 256) key_s[i] = score_key(score_of(c_lo + i));
-  if (sc_out != nullptr)
-    for (int c = tid; c < a.max_blocks; c += 256) sc_out[c] = score_of(c);
+  for (int i0 = 0; i0 < nc; i0 += 1024) {
+    float t[4];
+    scores4(c_lo + i0 + tid, c_lo + nc, t);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (i0 + u * 256 + tid < nc) key_s[i0 + u * 256 + tid] = score_key(t[u]);
+  }
+  if (sc_out != nullptr) {
+    for (int c0 = 0; c0 < a.max_blocks; c0 += 1024) {
+      float t[4];
+      scores4(c0 + tid, a.max_blocks, t);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (c0 + u * 256 + tid < a.max_blocks) sc_out[c0 + u * 256 + tid] = t[u];
+    }
+  }
   __syncthreads();
 
   // how many blocks have a score, and how many are chosen
@@ -315,24 +352,30 @@ __global__ __launch_bounds__(256) void select_blocks_kernel(SelectArgs a) {
   __syncthreads();
   const int m = m_total;
 
-  // segments: 0 = sink, 1..m = chosen blocks (their middle part), m+1 = window
+  // segments: 0 = sink, 1..m = chosen blocks (their middle part), then the
+  // window in up to kWindowSegs pieces, so that the waves share it
   const int s_end = min(a.n_sink, L);
   const int w_beg = max(a.n_sink, L - a.window);
+  const int w_len = L - w_beg;
+  const int n_wseg = max(1, min(kWindowSegs, (w_len + 255) / 256));
+  const int w_piece = (w_len + n_wseg - 1) / n_wseg;
+  const int n_seg = m + 1 + n_wseg;
   const uint8_t* pr = a.pad == nullptr ? nullptr : a.pad + (int64_t)b * a.pad_sb;
   auto seg_range = [&](int sgi, int* lo, int* hi) {
     if (sgi == 0) {
       *lo = 0;
       *hi = s_end;
-    } else if (sgi == m + 1) {
-      *lo = w_beg;
-      *hi = L;
+    } else if (sgi > m) {
+      const int k = sgi - m - 1;
+      *lo = w_beg + k * w_piece;
+      *hi = min(L, *lo + w_piece);
     } else {
       const int c = sel_s[sgi - 1];
       *lo = max(c * a.block, mid_lo);
       *hi = min((c + 1) * a.block, mid_hi);
     }
   };
-  for (int sgi = wave; sgi < m + 2; sgi += 4) {
+  for (int sgi = wave; sgi < n_seg; sgi += 4) {
     int lo, hi;
     seg_range(sgi, &lo, &hi);
     int cnt = 0;
@@ -345,7 +388,7 @@ __global__ __launch_bounds__(256) void select_blocks_kernel(SelectArgs a) {
   }
   __syncthreads();
   {   // segment counts -> offsets (each thread a contiguous run of segments)
-    const int nseg = m + 2, sch = (nseg + 255) / 256;
+    const int nseg = n_seg, sch = (nseg + 255) / 256;
     const int sb = min(nseg, tid * sch), se = min(nseg, sb + sch);
     int local = 0;
     for (int i = sb; i < se; ++i) local += segcnt_s[i];
@@ -360,7 +403,7 @@ __global__ __launch_bounds__(256) void select_blocks_kernel(SelectArgs a) {
   }
   __syncthreads();
   const int total = s_above;
-  for (int sgi = wave; sgi < m + 2; sgi += 4) {
+  for (int sgi = wave; sgi < n_seg; sgi += 4) {
     int lo, hi;
     seg_range(sgi, &lo, &hi);
     int base = segcnt_s[sgi];
