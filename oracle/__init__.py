@@ -11,7 +11,8 @@ Sources (page title, then the passage):
 * "Windowed-MTP: Removing the Full-Context Draft-KV Tax at Million-Token
   Context" (Pith review) -- "What carries the argument": the draft attends
   only to the first ``n_sink`` tokens plus the last ``W`` tokens; RoPE is
-  already inside the cached keys, so scores are plain dot products.
+  already inside the cached keys, so scores are plain dot products; the
+  draft KV pool can be compacted into a ring buffer.
 * "BudgetDraft: Acceptance-Aware Multi-View Training for Sparse-KV Speculative
   Decoding" (Pith review) -- abstract and Figure 2: the drafter reads a sparse
   KV view under a fixed budget, the verifier reads the full cache and produces
@@ -39,9 +40,10 @@ from .accept import argmax_ref, accept_ref, accept_bruteforce
 from .commit import commit_ref
 from .select import block_means_ref, block_scores_ref, select_blocks_ref
 from .partial import gather_ref, verify_mode_ref
+from .ring import ring_draft_ref, ring_from_logical, ring_slot
 
 __all__ = ["decode_bf16", "as_f64", "draft_view", "draft_attn_ref", "tree_depths",
            "tree_ancestors", "position_ids", "verify_keys", "verify_attn_ref",
            "argmax_ref", "accept_ref", "accept_bruteforce", "commit_ref",
            "block_means_ref", "block_scores_ref", "select_blocks_ref", "gather_ref",
-           "verify_mode_ref"]
+           "verify_mode_ref", "ring_draft_ref", "ring_from_logical", "ring_slot"]
