@@ -8,6 +8,7 @@
  *   spec_attn_draft_sparse  draft-phase attention over a sparse view of the KV
  *                           cache: attention sink + sliding window, or an
  *                           explicit budget list of positions.
+ *   spec_attn_draft_ring    the window draft over a draft-KV ring buffer.
  *   spec_attn_verify_tree   verify-phase attention of N speculated tree nodes
  *                           over the full cache plus their own tree, with
  *                           padded ragged batches and remapped positions.
@@ -168,6 +169,29 @@ spec_status spec_attn_draft_sparse(const spec_dims* dims, const void* q, int32_t
                                    int64_t idx_stride_b, int64_t idx_stride_h,
                                    void* out, float* lse_or_null,
                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Window draft over a draft-KV ring buffer ([WM] "What carries the
+ * argument": the draft KV working set is a constant window, so the draft KV
+ * pool compacts into a ring; the referee's remarks on its appendix name the
+ * slot mapping "ring base + logical position", wrapping, with a slack).
+ *
+ * The same attention as window mode of spec_attn_draft_sparse, but the
+ * cache holds only the sink and a ring: position p < n_sink lives in slot
+ * p, position p >= n_sink in slot n_sink + (p - n_sink) mod ring, and
+ * cache_len[b] is the sequence's logical length (it may exceed the ring
+ * cache's capacity).  The caller writes each new token's K/V at its slot,
+ * overwriting the position `ring` earlier.  ring >= window + n_q_tokens - 1
+ * (the chained queries reach back that far) and capacity >= n_sink + ring.
+ * cache_len[b] < n_q_tokens raises SPEC_DEV_CACHE_LEN.  Workspace as
+ * spec_draft_workspace_bytes(dims, n_q_tokens, n_sink + window + n_q_tokens
+ * - 1).
+ */
+spec_status spec_attn_draft_ring(const spec_dims* dims, const void* q, int32_t n_q_tokens,
+                                 const spec_kv* ring_cache, const int32_t* cache_len,
+                                 int32_t n_sink, int32_t window, int32_t ring, void* out,
+                                 float* lse_or_null, void* workspace, size_t workspace_bytes,
+                                 void* stream);
 
 /*
  * Tree-masked verify attention ([SM] "What carries the argument", Figure 9).

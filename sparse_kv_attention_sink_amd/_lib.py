@@ -34,7 +34,8 @@ SPEC_VERIFY_FULL = 0
 SPEC_VERIFY_PARTIAL = 1
 
 EXPORTED = [
-    "spec_attn_draft_sparse", "spec_attn_verify_tree", "spec_accept_greedy", "spec_kv_commit",
+    "spec_attn_draft_sparse", "spec_attn_draft_ring", "spec_attn_verify_tree",
+    "spec_accept_greedy", "spec_kv_commit",
     "spec_draft_workspace_bytes", "spec_verify_workspace_bytes", "spec_accept_workspace_bytes",
     "spec_commit_workspace_bytes", "spec_block_means", "spec_select_blocks",
     "spec_select_workspace_bytes", "spec_kv_gather", "spec_verify_mode",
@@ -75,6 +76,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     lib.spec_attn_draft_sparse.argtypes = [P, P, I32, P, P, I32, I32, P, I32, I64, I64, P, P, P, SZ, P]
     lib.spec_attn_draft_sparse.restype = I32
+    lib.spec_attn_draft_ring.argtypes = [P, P, I32, P, P, I32, I32, I32, P, P, P, SZ, P]
+    lib.spec_attn_draft_ring.restype = I32
     lib.spec_attn_verify_tree.argtypes = [P, P, I32, P, P, P, I64, P, P, I64, P, P, P, P, SZ, P]
     lib.spec_attn_verify_tree.restype = I32
     lib.spec_accept_greedy.argtypes = [I32, I32, I32, P, P, P, I64, I32, P, P, P, P, SZ, P]
@@ -206,6 +209,36 @@ def spec_attn_draft_sparse(q, k_cache, v_cache, cache_len, *, n_sink=0, window=0
                                     _ptr(cache_len), n_sink, window, _ptr(idx), budget, isb, ish,
                                     _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
                                     _stream(q))
+    _check(st)
+    return out, lse
+
+
+def spec_attn_draft_ring(q, k_ring, v_ring, cache_len, *, n_sink, window, ring, scale=None,
+                         out=None, lse=None, workspace=None, want_lse=True):
+    """Window draft over a ring cache ``[B, Hkv, >= n_sink + ring, D]``
+    (position p >= n_sink at slot n_sink + (p - n_sink) % ring); ``cache_len``
+    holds the logical lengths.  Returns (out, lse)."""
+    lib = load()
+    _on_gpu(q, k_ring, v_ring, cache_len)
+    if q.dim() != 4 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B, Tq, Hq, D] tensor")
+    B, Tq, Hq, D = q.shape
+    if k_ring.shape[0] != B or k_ring.shape[3] != D or q.dtype != k_ring.dtype:
+        raise ValueError("q and the ring cache disagree on batch, head_dim or dtype")
+    if cache_len.dtype != torch.int32 or cache_len.numel() != B or not cache_len.is_contiguous():
+        raise ValueError("cache_len must be a contiguous int32 [B] tensor")
+    kv = _kv(k_ring, v_ring)
+    dims = make_dims(B, Hq, k_ring.shape[1], D, _dtype_code(q), scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Tq, Hq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = new_workspace(draft_workspace_bytes(dims, Tq, n_sink + window + Tq - 1),
+                                  q.device)
+    st = lib.spec_attn_draft_ring(ctypes.byref(dims), _ptr(q), Tq, ctypes.byref(kv),
+                                  _ptr(cache_len), n_sink, window, ring, _ptr(out), _ptr(lse),
+                                  _ptr(workspace), workspace.numel(), _stream(q))
     _check(st)
     return out, lse
 

@@ -304,12 +304,14 @@ size_t spec_accept_workspace_bytes(int32_t batch, int32_t n_nodes, int32_t vocab
   return accept_bytes(batch, rows, accept_vsplits(rows, vocab));
 }
 
-spec_status spec_attn_draft_sparse(const spec_dims* dims, const void* q, int32_t n_q_tokens,
-                                   const spec_kv* cache, const int32_t* cache_len,
-                                   int32_t n_sink, int32_t window, const int32_t* idx,
-                                   int32_t budget, int64_t idx_stride_b, int64_t idx_stride_h,
-                                   void* out, float* lse_or_null, void* workspace,
-                                   size_t workspace_bytes, void* stream) {
+// Draft attention; kv_ring > 0 reads the window through a ring of that many
+// slots after the sink (validated by the caller).
+static spec_status draft_impl(const spec_dims* dims, const void* q, int32_t n_q_tokens,
+                              const spec_kv* cache, const int32_t* cache_len, int32_t n_sink,
+                              int32_t window, const int32_t* idx, int32_t budget,
+                              int64_t idx_stride_b, int64_t idx_stride_h, int32_t kv_ring,
+                              void* out, float* lse_or_null, void* workspace,
+                              size_t workspace_bytes, void* stream) {
   spec_status st = check_dims(dims);
   if (st != SPEC_OK) return st;
   if (n_q_tokens < 1) return fail(SPEC_E_INVALID, "n_q_tokens %d < 1", n_q_tokens);
@@ -358,6 +360,7 @@ spec_status spec_attn_draft_sparse(const spec_dims* dims, const void* q, int32_t
   a.scale_log2 = dims->softmax_scale * kLog2e;
   a.n_sink = n_sink;
   a.window = window;
+  a.kv_ring = kv_ring;
   a.idx = idx;
   a.budget = budget;
   a.idx_sb = idx_stride_b;
@@ -377,6 +380,35 @@ spec_status spec_attn_draft_sparse(const spec_dims* dims, const void* q, int32_t
       return hip_fail(e, "combine launch");
   }
   return SPEC_OK;
+}
+
+spec_status spec_attn_draft_sparse(const spec_dims* dims, const void* q, int32_t n_q_tokens,
+                                   const spec_kv* cache, const int32_t* cache_len,
+                                   int32_t n_sink, int32_t window, const int32_t* idx,
+                                   int32_t budget, int64_t idx_stride_b, int64_t idx_stride_h,
+                                   void* out, float* lse_or_null, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  return draft_impl(dims, q, n_q_tokens, cache, cache_len, n_sink, window, idx, budget,
+                    idx_stride_b, idx_stride_h, 0, out, lse_or_null, workspace, workspace_bytes,
+                    stream);
+}
+
+spec_status spec_attn_draft_ring(const spec_dims* dims, const void* q, int32_t n_q_tokens,
+                                 const spec_kv* ring_cache, const int32_t* cache_len,
+                                 int32_t n_sink, int32_t window, int32_t ring, void* out,
+                                 float* lse_or_null, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  spec_status st = check_dims(dims);
+  if (st != SPEC_OK) return st;
+  if (n_q_tokens < 1) return fail(SPEC_E_INVALID, "n_q_tokens %d < 1", n_q_tokens);
+  if (n_sink < 0 || window < 1) return fail(SPEC_E_INVALID, "need n_sink >= 0 and window >= 1");
+  if ((int64_t)ring < (int64_t)window + n_q_tokens - 1)
+    return fail(SPEC_E_INVALID, "ring %d < window + n_q_tokens - 1 (%lld)", ring,
+                (long long)window + n_q_tokens - 1);
+  if (ring_cache != nullptr && (int64_t)ring_cache->capacity < (int64_t)n_sink + ring)
+    return fail(SPEC_E_INVALID, "ring cache capacity %d < n_sink + ring", ring_cache->capacity);
+  return draft_impl(dims, q, n_q_tokens, ring_cache, cache_len, n_sink, window, nullptr, 0, 0, 0,
+                    ring, out, lse_or_null, workspace, workspace_bytes, stream);
 }
 
 spec_status spec_attn_verify_tree(const spec_dims* dims, const void* q, int32_t n_nodes,

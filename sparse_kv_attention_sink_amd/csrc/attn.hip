@@ -90,7 +90,14 @@ struct KeySrc {
   uint32_t rowb, trowb;     // row strides in bytes
   uint32_t kbytes, tbytes;  // addressable bytes from k / tk
   int n_view, cache_tiles, n_tree, s_len, w_start, v0;
+  int kv_ring, n_sink;      // window through a ring: slot n_sink + (p - n_sink) % kv_ring
 };
+
+// Row of key position p: p itself, or its ring slot when the window is kept
+// in a ring after the sink.
+__device__ __forceinline__ int ring_row(KeySrc ks, int p) {
+  return (ks.kv_ring == 0 || p < ks.n_sink) ? p : ks.n_sink + (p - ks.n_sink) % ks.kv_ring;
+}
 
 // Key position of view position v (0 <= v < n_view).
 template <int MODE>
@@ -108,7 +115,10 @@ __device__ __forceinline__ bool is_tree_tile(KeySrc ks, int t, int mode) {
 // row (keys past the end re-read it; their scores are masked).
 template <int MODE>
 __device__ __forceinline__ int tile_row(KeySrc ks, int t, int r) {
-  if (!is_tree_tile(ks, t, MODE)) return view_pos<MODE>(ks, min(t * kTileKeys + r, ks.n_view - 1));
+  if (!is_tree_tile(ks, t, MODE)) {
+    const int p = view_pos<MODE>(ks, min(t * kTileKeys + r, ks.n_view - 1));
+    return MODE == kDraftWindow ? ring_row(ks, p) : p;
+  }
   return min((t - ks.cache_tiles) * kTileKeys + r, ks.n_tree - 1);
 }
 
@@ -125,7 +135,12 @@ __device__ __forceinline__ int tile_first_row(KeySrc ks, int t) {
   if (v + kTileKeys > ks.n_view) return -1;
   if constexpr (MODE == kDraftWindow) {
     if (v + kTileKeys <= ks.s_len) return v;
-    if (v >= ks.s_len) return ks.w_start + (v - ks.s_len);
+    if (v >= ks.s_len) {
+      const int p0 = ks.w_start + (v - ks.s_len);
+      if (ks.kv_ring == 0 || p0 < ks.n_sink) return p0;
+      const int off = (p0 - ks.n_sink) % ks.kv_ring;   // a tile across the ring's end is gathered
+      return off + kTileKeys <= ks.kv_ring ? ks.n_sink + off : -1;
+    }
     return -1;
   } else if constexpr (MODE == kDraftGather) {
     return -1;
@@ -358,7 +373,8 @@ void attn_bf16_kernel(AttnArgs a) {
   const int T = a.T, G = a.G, N = a.T;
 
   const int L = a.cache_len[b];
-  bool bad = MODE == kVerify ? (L < 0 || L > a.capacity) : (L < T || L > a.capacity);
+  bool bad = MODE == kVerify ? (L < 0 || L > a.capacity)
+                             : (L < T || (a.kv_ring == 0 && L > a.capacity));   // a ring keeps the logical length
   if (leader && tid == 0 && bad) raise_error(a.err, SPEC_DEV_CACHE_LEN);
 
   // ---------------------------------------------------------------- tree
@@ -516,6 +532,8 @@ void attn_bf16_kernel(AttnArgs a) {
   ks.s_len = s_len;
   ks.w_start = w_start;
   ks.v0 = t0 * kTileKeys;
+  ks.kv_ring = MODE == kDraftWindow ? a.kv_ring : 0;
+  ks.n_sink = a.n_sink;
   const uint32_t ring_base = lds_addr(ring) + kgi * (WK == 1 ? NS : 1) * SB;
   const int wl = WK == 1 ? wave : 0;   // index of this wavefront among the loaders
 

@@ -115,7 +115,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
   int L = a.cache_len[b];
   bool bad;
   if (MODE == kVerify) bad = a.bad[b] != 0;
-  else bad = L < a.T || L > a.capacity;
+  else bad = L < a.T || (a.kv_ring == 0 && L > a.capacity);   // a ring keeps the logical length
   if (bad) L = 0;
 
   __shared__ float qs[128];
@@ -157,8 +157,9 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
       if (MODE == kDraftWindow) {
         const int j = pos < s_len ? pos : w_start + (pos - s_len);
         vis = j < e && (j < a.n_sink || j >= e - a.window);
-        krow = kc + (int64_t)j * a.kt;
-        vrow = vc + (int64_t)j * a.kt;
+        const int jr = (a.kv_ring == 0 || j < a.n_sink) ? j : a.n_sink + (j - a.n_sink) % a.kv_ring;
+        krow = kc + (int64_t)jr * a.kt;
+        vrow = vc + (int64_t)jr * a.kt;
       } else if (MODE == kDraftGather) {
         const int j = a.idx[b * a.idx_sb + g * a.idx_sh + pos];
         if (j == -1) {          // padding entry: selects nothing

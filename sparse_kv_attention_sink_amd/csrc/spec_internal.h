@@ -49,6 +49,7 @@ struct AttnArgs {
   float scale_log2;                 // softmax_scale * log2(e)
   // draft
   int32_t n_sink, window;
+  int32_t kv_ring;                  // > 0: the window is read through a ring of this many slots
   const int32_t* idx;
   int32_t budget;
   int64_t idx_sb, idx_sh;

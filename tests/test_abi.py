@@ -286,6 +286,25 @@ def test_verify_mode_follows_the_schedule_table(lib):
     assert lib.spec_verify_mode(100, 4096, 0, 0, 64) == skg.SPEC_E_INVALID
 
 
+def ring_call(lib, d, *, tq=1, cache=None, sink=4, win=64, ring=64, ws=FAKE, wsb=1 << 30):
+    cache = cache or kv(cap=68)
+    return lib.spec_attn_draft_ring(ctypes.byref(d), FAKE, tq, ctypes.byref(cache), FAKE, sink,
+                                    win, ring, FAKE, None, ws, wsb, None)
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(ring=63), skg.SPEC_E_INVALID),                      # < window + Tq - 1
+    (dict(tq=3, ring=65), skg.SPEC_E_INVALID),
+    (dict(cache=kv(cap=67)), skg.SPEC_E_INVALID),             # < n_sink + ring
+    (dict(win=0), skg.SPEC_E_INVALID),
+    (dict(sink=-1), skg.SPEC_E_INVALID),
+    (dict(tq=0), skg.SPEC_E_INVALID),
+    (dict(ws=None), skg.SPEC_E_WORKSPACE),
+])
+def test_ring_draft_rejects_bad_arguments(lib, bad, status):
+    assert ring_call(lib, dims(), **bad) == status
+
+
 def test_device_status_rejects_null(lib):
     assert lib.spec_device_status(None, None, None) == skg.SPEC_E_INVALID
 
