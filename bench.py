@@ -436,6 +436,74 @@ def run_partial_1m(torch, skg, layers, *, block=128, budget=4096, buffer=64, win
                              "the gather of the partial cache")
 
 
+# ------------------------------------------------------------ draft ring buffer
+
+def run_ring_1m(torch, skg, layers, *, reps=3):
+    """The 1M step's drafts (per layer one 3-query context call and three
+    single-query calls, sink 4 + window 4096) over per-layer ring caches of
+    4 + 4,098 slots, against the same calls over the full caches; each timed
+    as a pass over the 32 layers with only its bracketing events."""
+    dev = torch.device("cuda:0")
+    cl = torch.tensor([L1M], dtype=torch.int32, device=dev)
+    ring = WINDOW + CHAIN - 1
+    pos = torch.arange(L1M - ring, L1M, device=dev)
+    slots = SINK + (pos - SINK) % ring
+    rings = []
+    for lay in layers:
+        kr = torch.empty((1, HKV, SINK + ring, D), dtype=torch.bfloat16, device=dev)
+        vr = torch.empty_like(kr)
+        kr[:, :, :SINK] = lay["k"][:, :, :SINK]
+        vr[:, :, :SINK] = lay["v"][:, :, :SINK]
+        kr[:, :, slots] = lay["k"][:, :, pos]
+        vr[:, :, slots] = lay["v"][:, :, pos]
+        rings.append((kr, vr))
+    dims = skg.make_dims(1, HQ, HKV, D, skg.SPEC_BF16)
+    ws_c = skg.new_workspace(skg.draft_workspace_bytes(dims, CHAIN, SINK + WINDOW + CHAIN - 1), dev)
+    ws_f = skg.new_workspace(skg.draft_workspace_bytes(dims, 1, SINK + WINDOW), dev)
+    out_c = torch.empty((1, CHAIN, HQ, D), dtype=torch.bfloat16, device=dev)
+    out_f = torch.empty((1, 1, HQ, D), dtype=torch.bfloat16, device=dev)
+
+    def ring_pass():
+        for lay, (kr, vr) in zip(layers, rings):
+            skg.spec_attn_draft_ring(lay["ctx_q"], kr, vr, cl, n_sink=SINK, window=WINDOW,
+                                     ring=ring, out=out_c, want_lse=False, workspace=ws_c)
+            for fq in lay["fwd_q"]:
+                skg.spec_attn_draft_ring(fq, kr, vr, cl, n_sink=SINK, window=WINDOW, ring=ring,
+                                         out=out_f, want_lse=False, workspace=ws_f)
+
+    def full_pass():
+        for lay in layers:
+            skg.spec_attn_draft_sparse(lay["ctx_q"], lay["k"], lay["v"], cl, n_sink=SINK,
+                                       window=WINDOW, out=out_c, want_lse=False, workspace=ws_c)
+            for fq in lay["fwd_q"]:
+                skg.spec_attn_draft_sparse(fq, lay["k"], lay["v"], cl, n_sink=SINK, window=WINDOW,
+                                           out=out_f, want_lse=False, workspace=ws_f)
+
+    res = {}
+    for name, fn in (("ring", ring_pass), ("full_cache", full_pass)):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        prerecord([a, b], torch)
+        torch.cuda._sleep(int(3e7))
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        res[name] = a.elapsed_time(b) / reps * 1e3 / len(layers)
+    for w in (ws_c, ws_f):
+        assert skg.spec_device_status(w) == 0
+    del rings
+    torch.cuda.empty_cache()
+    row = 2 * D * 2 * HKV
+    return dict(ring_slots=SINK + ring, draft_us_per_layer_ring=round(res["ring"], 2),
+                draft_us_per_layer_full_cache=round(res["full_cache"], 2),
+                draft_kv_bytes_per_layer_ring=(SINK + ring) * row,
+                draft_kv_bytes_per_layer_full=L1M * row,
+                note="per layer: one 3-query context call and three single-query calls")
+
+
 # ------------------------------------------------------------ budget selection
 
 def run_select(torch, skg, *, B=8, L=16384, block=16, reps=24, seed=8400):
@@ -642,6 +710,9 @@ def main():
     if not args.skip_cpu:
         cpu = cpu_baseline(layers, torch)
         log(f"[bench] cpu oracle: {cpu['value']:.3f} GB/s")
+    ring = run_ring_1m(torch, skg, layers)
+    log(f"[bench] ring drafts: {ring['draft_us_per_layer_ring']} us per layer "
+        f"(full cache {ring['draft_us_per_layer_full_cache']} us)")
     partial = run_partial_1m(torch, skg, layers)
     partial["verify_full_us_per_layer"] = round(r1m["verify_avg_ms"] * 1e3, 2)
     log(f"[bench] partial verify: {partial['verify_partial_us_per_layer']} us per layer "
@@ -695,6 +766,7 @@ def main():
         "kv_commit": commit,
         "budget_select": select,
         "partial_verify_1m": partial,
+        "ring_draft_1m": ring,
     }
     print(json.dumps(line), flush=True)
 
