@@ -12,8 +12,9 @@ as t_verify + t_ctx_draft + 3 t_fwd_draft (per layer) + t_accept.
 Reported: algorithmic KV bytes per step / step time (GB/s, against the 8 TB/s
 HBM peak), steps per second, the per-component times, the roofline position
 of the dominant kernel (verify) measured with HIP events on the launch
-stream, the 16K-context batch-8 step per draft budget, and the fp64 CPU
-oracle timed on a bounded sample of the same workload.
+stream, the 16K-context batch-8 step per draft budget, the 4K-context
+step and the ragged batch of 16 with its 44- and 64-node trees, and the fp64
+CPU oracle timed on a bounded sample of the same workload.
 
 Inputs are seeded synthetic draws (no datasets, no weights); everything is
 resident on the GPU before the timed region starts.
@@ -289,6 +290,157 @@ def run_16k(args, torch, skg):
         )
     for w in (ws_v, ws_a):
         assert skg.spec_device_status(w) == 0
+    del kvs
+    torch.cuda.empty_cache()
+    return out
+
+
+# ------------------------------------------------------------ 4K and ragged workloads
+
+def _timed_steps(torch, step, n_steps, n_marks):
+    """Time n_steps calls of step(i) back to back (two events around the
+    loop), then an instrumented pass whose n_marks events per step give the
+    per-call breakdown (events between kernels idle the GPU for a few
+    microseconds each, so the two are kept apart)."""
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    for i in range(2):
+        step(i)
+    torch.cuda.synchronize()
+    a, b = ev(), ev()
+    a.record()
+    for i in range(n_steps):
+        step(i)
+    b.record()
+    torch.cuda.synchronize()
+    ms_step = a.elapsed_time(b) / n_steps
+    marks = [[ev() for _ in range(n_marks)] for _ in range(n_steps)]
+    prerecord([e for m in marks for e in m], torch)
+    for i, m in enumerate(marks):
+        step(i, m)
+    torch.cuda.synchronize()
+    parts = [sum(m[k].elapsed_time(m[k + 1]) for m in marks) / n_steps for k in range(n_marks - 1)]
+    return ms_step, parts
+
+
+def run_4k(args, torch, skg):
+    """Llama-3-8B-shaped layer at 4K context, batch 1: t_verify(chain of 5) +
+    5 t_draft(budget 256) + t_accept over 6 x 128256 logits.  The KV of one
+    layer is 16.8 MB, so the step rotates over 64 layers' KV (1.07 GB) and the
+    Infinity Cache does not serve the reads."""
+    import numpy as np
+    import synth
+    dev = torch.device("cuda:0")
+    Bsz, L, ROT, GAMMA, BUD = 1, 4096, 64, 5, 256
+    s = 1.0 / math.sqrt(D)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(synth.SEEDS[2] + 500)
+    kvs = [tuple((torch.randn((Bsz, HKV, L, D), generator=gen, device=dev) * s).to(torch.bfloat16)
+                 for _ in range(2)) for _ in range(ROT)]
+    tree = synth.chain_tree(GAMMA)
+    parents = torch.from_numpy(tree.parents).to(dev)
+    vq = (torch.randn((Bsz, GAMMA, HQ, D), generator=gen, device=dev) * s).to(torch.bfloat16)
+    tk = (torch.randn((Bsz, HKV, GAMMA, D), generator=gen, device=dev) * s).to(torch.bfloat16)
+    tv = (torch.randn((Bsz, HKV, GAMMA, D), generator=gen, device=dev) * s).to(torch.bfloat16)
+    dq = (torch.randn((Bsz, 1, HQ, D), generator=gen, device=dev) * s).to(torch.bfloat16)
+    cache_len = torch.full((Bsz,), L, dtype=torch.int32, device=dev)
+    logits = torch.randn((Bsz, GAMMA + 1, VOCAB), generator=gen, device=dev)
+    tokens = torch.randint(0, VOCAB, (Bsz, GAMMA), generator=gen, device=dev, dtype=torch.int32)
+    idx = torch.from_numpy(synth.budget_indices(np.random.default_rng(synth.SEEDS[2] + 1), L, BUD)
+                           [None, None, :]).to(dev)
+    dims = skg.make_dims(Bsz, HQ, HKV, D, skg.SPEC_BF16)
+    ws_v = skg.new_workspace(skg.verify_workspace_bytes(dims, GAMMA, L), dev)
+    ws_d = skg.new_workspace(skg.draft_workspace_bytes(dims, 1, BUD), dev)
+    ws_a = skg.new_workspace(skg.accept_workspace_bytes(Bsz, GAMMA, VOCAB), dev)
+
+    def step(i, marks=None):
+        k, v = kvs[(i * 6) % ROT]
+        if marks: marks[0].record()
+        skg.spec_attn_verify_tree(vq, k, v, cache_len, tk, tv, parents, workspace=ws_v)
+        if marks: marks[1].record()
+        for j in range(GAMMA):
+            k2, v2 = kvs[(i * 6 + 1 + j) % ROT]
+            skg.spec_attn_draft_sparse(dq, k2, v2, cache_len, idx=idx, workspace=ws_d)
+        if marks: marks[2].record()
+        skg.spec_accept_greedy(logits, tokens, parents, GAMMA, workspace=ws_a)
+        if marks: marks[3].record()
+
+    n_steps = max(args.steps, 4) * 8
+    ms_step, (tv_ms, td5_ms, ta_ms) = _timed_steps(torch, step, n_steps, 4)
+    vb = verify_bytes(Bsz, L, GAMMA)
+    db = draft_bytes(Bsz, L, 1, BUD) + BUD * 4
+    ab = accept_bytes(Bsz, GAMMA, VOCAB)
+    for w in (ws_v, ws_d, ws_a):
+        assert skg.spec_device_status(w) == 0
+    del kvs
+    torch.cuda.empty_cache()
+    return dict(context=L, batch=Bsz, verify=f"chain of {GAMMA}", draft_budget=BUD,
+                ms_step=round(ms_step, 4), steps_per_s=round(1e3 / ms_step, 1),
+                gbs=round((vb + GAMMA * db + ab) / (ms_step * 1e-3) / 1e9, 1),
+                t_verify_us=round(tv_ms * 1e3, 2), t_draft_us=round(td5_ms * 1e3 / GAMMA, 2),
+                t_accept_us=round(ta_ms * 1e3, 2),
+                verify_gbs=round(vb / (tv_ms * 1e-3) / 1e9, 1),
+                draft_gbs=round(db * GAMMA / (td5_ms * 1e-3) / 1e9, 1),
+                accept_gbs=round(ab / (ta_ms * 1e-3) / 1e9, 1))
+
+
+def run_ragged(args, torch, skg):
+    """Batch of 16 with contexts drawn from U{2048..32768} and the tail pad
+    pattern (the last 32 verify steps of 5 slots each, part of each group
+    padding), for the 44-node (widths 10/14/12/8) and the 64-node
+    (10/18/18/18) trees: t_verify + t_accept over 16 x (N+1) x 128256 logits.
+    The KV (about 1.2 GB read per verify) rotates over 4 copies."""
+    import numpy as np
+    import synth
+    dev = torch.device("cuda:0")
+    Bsz, HI, ROT = 16, 32768, 4
+    s = 1.0 / math.sqrt(D)
+    rng = np.random.default_rng(synth.SEEDS[5])
+    lens = rng.integers(2048, HI + 1, size=Bsz).astype(np.int32)
+    pad_np = np.zeros((Bsz, HI), dtype=np.uint8)
+    for b in range(Bsz):
+        pad_np[b, :lens[b]] = synth.pad_groups(rng, int(lens[b]))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(synth.SEEDS[5] + 500)
+    kvs = [tuple((torch.randn((Bsz, HKV, HI, D), generator=gen, device=dev) * s).to(torch.bfloat16)
+                 for _ in range(2)) for _ in range(ROT)]
+    cache_len = torch.from_numpy(lens).to(dev)
+    pad = torch.from_numpy(pad_np).to(dev)
+    dims = skg.make_dims(Bsz, HQ, HKV, D, skg.SPEC_BF16)
+    L_sum = int(lens.sum())
+    out = {"batch": Bsz, "context_sum": L_sum, "pad_slots": int(pad_np.sum())}
+    for name, widths in (("tree44", (10, 14, 12, 8)), ("tree64", (10, 18, 18, 18))):
+        tree = synth.layered_tree(rng, widths)
+        N = tree.n
+        parents = torch.from_numpy(tree.parents).to(dev)
+        vq = (torch.randn((Bsz, N, HQ, D), generator=gen, device=dev) * s).to(torch.bfloat16)
+        tk = (torch.randn((Bsz, HKV, N, D), generator=gen, device=dev) * s).to(torch.bfloat16)
+        tv = (torch.randn((Bsz, HKV, N, D), generator=gen, device=dev) * s).to(torch.bfloat16)
+        logits = torch.randn((Bsz, N + 1, VOCAB), generator=gen, device=dev)
+        tokens = torch.randint(0, VOCAB, (Bsz, N), generator=gen, device=dev, dtype=torch.int32)
+        ws_v = skg.new_workspace(skg.verify_workspace_bytes(dims, N, HI), dev)
+        ws_a = skg.new_workspace(skg.accept_workspace_bytes(Bsz, N, VOCAB), dev)
+
+        def step(i, marks=None):
+            k, v = kvs[i % ROT]
+            if marks: marks[0].record()
+            skg.spec_attn_verify_tree(vq, k, v, cache_len, tk, tv, parents, pad=pad, workspace=ws_v)
+            if marks: marks[1].record()
+            skg.spec_accept_greedy(logits, tokens, parents, 4, workspace=ws_a)
+            if marks: marks[2].record()
+
+        n_steps = max(args.steps, 4) * 2
+        ms_step, (tv_ms, ta_ms) = _timed_steps(torch, step, n_steps, 3)
+        vb = verify_bytes(Bsz, L_sum, N, pad=True)
+        ab = accept_bytes(Bsz, N, VOCAB)
+        for w in (ws_v, ws_a):
+            assert skg.spec_device_status(w) == 0
+        out[name] = dict(nodes=N, ms_step=round(ms_step, 4), steps_per_s=round(1e3 / ms_step, 1),
+                         gbs=round((vb + ab) / (ms_step * 1e-3) / 1e9, 1),
+                         t_verify_us=round(tv_ms * 1e3, 2), t_accept_us=round(ta_ms * 1e3, 2),
+                         verify_gbs=round(vb / (tv_ms * 1e-3) / 1e9, 1),
+                         verify_tflops=round(4 * D * HQ * N * L_sum / (tv_ms * 1e-3) / 1e12, 1),
+                         accept_gbs=round(ab / (ta_ms * 1e-3) / 1e9, 1))
+        del logits
     del kvs
     torch.cuda.empty_cache()
     return out
@@ -720,6 +872,11 @@ def main():
     del layers
     torch.cuda.empty_cache()
     r16 = None if args.skip_16k else run_16k(args, torch, skg)
+    r4k = run_4k(args, torch, skg)
+    log(f"[bench] 4K step: {r4k['ms_step']} ms ({r4k['steps_per_s']} steps/s)")
+    rrag = run_ragged(args, torch, skg)
+    log(f"[bench] ragged batch: tree44 {rrag['tree44']['ms_step']} ms, "
+        f"tree64 {rrag['tree64']['ms_step']} ms")
     commit = {
         "16k_batch8_tree64": run_commit(torch, skg, B=8, L=16384, widths=(10, 18, 18, 18),
                                         depths=[4, 3, 2, 1, 0, 4, 2, 3], seed=8300),
@@ -763,6 +920,8 @@ def main():
                      "avg_launch_ms": round(v_ms, 4)},
         "cpu_baseline": cpu,
         "ctx16k": r16,
+        "ctx4k": r4k,
+        "ragged": rrag,
         "kv_commit": commit,
         "budget_select": select,
         "partial_verify_1m": partial,

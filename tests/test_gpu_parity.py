@@ -170,6 +170,7 @@ SHAPES = [
     (2, 8, 2, 128, 517, [517, 203], "bf16"),
     (2, 6, 2, 128, 97, [97, 5], "f32"),
     (1, 8, 8, 64, 1000, [1000], "bf16"),
+    (2, 16, 2, 128, 700, [700, 333], "bf16"),   # GQA 8: a 44-node tree has 352 rows per KV head
 ]
 
 
