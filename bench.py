@@ -69,6 +69,32 @@ def accept_bytes(B, N, V):
     return B * (N + 1) * V * 4 + B * N * 4 * 2
 
 
+# ------------------------------------------------------------ HIP graphs
+
+def graph_replay_ms(torch, fn, reps):
+    """Capture fn() (a sequence of library calls on the current stream) into
+    one HIP graph and return the device time per replay over `reps` replays
+    bracketed by two events: the step without host launch costs."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fn()
+    graph.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        graph.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps, graph
+
+
 # ------------------------------------------------------------ 1M workload
 
 def prerecord(events, torch):
@@ -166,6 +192,26 @@ def run_1m(args, torch, skg):
     torch.cuda.synchronize()
     ms_step_marked = a.elapsed_time(b) / args.steps
 
+    # The same step captured in a HIP graph and replayed.  A replay must
+    # reproduce the eager step's integer outputs (position ids, acceptance)
+    # exactly and its attention outputs within rounding: the long verify
+    # splits take their tile chunks from a shared pool at run time, so the
+    # order of the fp32 sums, and with it the last bit, can differ.
+    step()
+    torch.cuda.synchronize()
+    att = (v_out, v_lse, c_out, c_lse, f_out, f_lse)
+    ints = (v_pos, *acc)
+    eager_att = [t.float().clone() for t in att]
+    eager_int = [t.clone() for t in ints]
+    for t in att:
+        t.fill_(0)
+    graph_ms, graph = graph_replay_ms(torch, step, args.steps)
+    graph_ints_equal = all(bool(torch.equal(x, y)) for x, y in zip(eager_int, ints))
+    graph_att_diff = max(float((x - y.float()).abs().max()) for x, y in zip(eager_att, att))
+    del graph
+    for w in (ws_v, ws_c, ws_f, ws_a):
+        assert skg.spec_device_status(w) == 0, "device range error in the graph replays"
+
     t_verify = [m[0].elapsed_time(m[1]) for st in marks for m in st]
     t_ctx = [m[1].elapsed_time(m[2]) for st in marks for m in st]
     t_fwd = [m[2].elapsed_time(m[3]) / CHAIN for st in marks for m in st]
@@ -195,6 +241,10 @@ def run_1m(args, torch, skg):
                            fwd_draft_per_call=sum(t_fwd) / len(t_fwd)),
         call_gbs=dict(verify=v_gbs, ctx_draft=ctx_gbs, fwd_draft=fwd_gbs),
         verify_bytes_per_launch=vb, verify_avg_ms=v_avg_ms,
+        graph=dict(ms_step=graph_ms, steps_per_s=1e3 / graph_ms,
+                   gbs=step_bytes / (graph_ms * 1e-3) / 1e9,
+                   replay_int_outputs_equal=graph_ints_equal,
+                   replay_attn_max_abs_diff=graph_att_diff),
     )
     return res, layers
 
@@ -277,10 +327,15 @@ def run_16k(args, torch, skg):
         tv_ms = sum(m[0].elapsed_time(m[1]) for m in marks) / len(marks)
         td_ms = sum(m[1].elapsed_time(m[2]) for m in marks) / len(marks) / 4
         ta_ms = sum(m[2].elapsed_time(m[3]) for m in marks) / len(marks)
+        # HIP graph of 16 consecutive steps (one rotation cycle), replayed
+        g_ms, graph = graph_replay_ms(torch, lambda: [step(i * 5) for i in range(ROT)], max(reps // 4, 2))
+        del graph
+        g_ms /= ROT
         vb = verify_bytes(Bsz, Bsz * L, N)
         db = draft_bytes(Bsz, L, 1, bud) + Bsz * bud * 4
         ab = accept_bytes(Bsz, N, VOCAB)
         out[str(bud)] = dict(
+            graph_ms_step=g_ms, graph_steps_per_s=1e3 / g_ms,
             ms_step=ms_step, steps_per_s=1e3 / ms_step,
             gbs=(vb + 4 * db + ab) / (ms_step * 1e-3) / 1e9,
             t_verify_ms=tv_ms, t_draft_ms=td_ms, t_accept_ms=ta_ms,
@@ -366,6 +421,10 @@ def run_4k(args, torch, skg):
 
     n_steps = max(args.steps, 4) * 8
     ms_step, (tv_ms, td5_ms, ta_ms) = _timed_steps(torch, step, n_steps, 4)
+    # HIP graph of 32 consecutive steps (three rotation cycles), replayed
+    g_ms, graph = graph_replay_ms(torch, lambda: [step(i) for i in range(32)], max(args.steps, 4))
+    del graph
+    g_ms /= 32
     vb = verify_bytes(Bsz, L, GAMMA)
     db = draft_bytes(Bsz, L, 1, BUD) + BUD * 4
     ab = accept_bytes(Bsz, GAMMA, VOCAB)
@@ -376,6 +435,7 @@ def run_4k(args, torch, skg):
     return dict(context=L, batch=Bsz, verify=f"chain of {GAMMA}", draft_budget=BUD,
                 ms_step=round(ms_step, 4), steps_per_s=round(1e3 / ms_step, 1),
                 gbs=round((vb + GAMMA * db + ab) / (ms_step * 1e-3) / 1e9, 1),
+                graph_ms_step=round(g_ms, 4), graph_steps_per_s=round(1e3 / g_ms, 1),
                 t_verify_us=round(tv_ms * 1e3, 2), t_draft_us=round(td5_ms * 1e3 / GAMMA, 2),
                 t_accept_us=round(ta_ms * 1e3, 2),
                 verify_gbs=round(vb / (tv_ms * 1e-3) / 1e9, 1),
@@ -430,11 +490,15 @@ def run_ragged(args, torch, skg):
 
         n_steps = max(args.steps, 4) * 2
         ms_step, (tv_ms, ta_ms) = _timed_steps(torch, step, n_steps, 3)
+        g_ms, graph = graph_replay_ms(torch, lambda: [step(i) for i in range(ROT)], max(args.steps // 2, 2))
+        del graph
+        g_ms /= ROT
         vb = verify_bytes(Bsz, L_sum, N, pad=True)
         ab = accept_bytes(Bsz, N, VOCAB)
         for w in (ws_v, ws_a):
             assert skg.spec_device_status(w) == 0
         out[name] = dict(nodes=N, ms_step=round(ms_step, 4), steps_per_s=round(1e3 / ms_step, 1),
+                         graph_ms_step=round(g_ms, 4), graph_steps_per_s=round(1e3 / g_ms, 1),
                          gbs=round((vb + ab) / (ms_step * 1e-3) / 1e9, 1),
                          t_verify_us=round(tv_ms * 1e3, 2), t_accept_us=round(ta_ms * 1e3, 2),
                          verify_gbs=round(vb / (tv_ms * 1e-3) / 1e9, 1),
@@ -911,6 +975,7 @@ def main():
                    "verify": "3-token chain over the full cache per layer", "vocab": VOCAB},
         "pct_of_hbm_peak": round(100 * r1m["gbs"] / HBM_PEAK_GBS, 2),
         "steps_per_s": round(r1m["steps_per_s"], 3),
+        "graph": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r1m["graph"].items()},
         "components_ms": {k: round(v, 4) for k, v in r1m["components_ms"].items()},
         "call_gbs": {k: round(v, 1) for k, v in r1m["call_gbs"].items()},
         "roofline": {"kernel": "verify (chain 3 over 1,048,576 keys, 8 KV heads)",
