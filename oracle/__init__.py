@@ -37,7 +37,7 @@ from .bf16 import decode_bf16, as_f64
 from .attention import (draft_view, draft_attn_ref, tree_depths, tree_ancestors,
                         position_ids, verify_keys, verify_attn_ref)
 from .accept import argmax_ref, accept_ref, accept_bruteforce
-from .commit import commit_ref
+from .commit import commit_ref, compact_ref
 from .select import block_means_ref, block_scores_ref, select_blocks_ref
 from .partial import gather_ref, verify_mode_ref
 from .ring import ring_draft_ref, ring_from_logical, ring_slot

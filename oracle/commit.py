@@ -83,3 +83,39 @@ def commit_ref(k, v, cache_len, pad, tree_k, tree_v, accept_len, accept_path, ma
             pad[b, L + j] = 0 if j <= tau else 1
         cache_len[b] = L + P
     return k, v, cache_len, pad, P, err
+
+
+def compact_ref(k, v, cache_len, pad):
+    """Drop the padding slots of each sequence's cache (the pads that batched
+    commits leave behind; SpecPV section 3.3 removes the tokens that were not
+    accepted once verification is done, SpecMemo Figure 9 pads per step).
+
+    Reading of what the pages leave open: the valid slots j < cache_len[b]
+    (pad byte 0) keep their order and move to slots 0, 1, ...; cache_len[b]
+    becomes their count; every pad byte below the old cache_len is cleared.
+    The contents of the slots from the new cache_len on are left unspecified
+    (here: as they were).  A sequence whose cache_len lies outside
+    [0, capacity] is left as it is and the error is reported (bit 1).
+
+    ``k``, ``v``: ``[B, Hkv, L_cap, D]``; ``cache_len`` ``[B]``; ``pad``
+    ``[B, >= L_cap]`` uint8.  Returns new arrays ``(k, v, cache_len, pad,
+    err)``.
+    """
+    k = np.array(k, copy=True)
+    v = np.array(v, copy=True)
+    pad = np.array(pad, copy=True)
+    cache_len = np.array(cache_len, dtype=np.int64, copy=True)
+    cap = k.shape[2]
+    err = 0
+    for b in range(len(cache_len)):
+        L = int(cache_len[b])
+        if L < 0 or L > cap:
+            err |= ERR_CACHE_LEN
+            continue
+        keep = np.nonzero(pad[b, :L] == 0)[0]
+        n = len(keep)
+        k[b][:, :n] = k[b][:, keep]
+        v[b][:, :n] = v[b][:, keep]
+        pad[b, :L] = 0
+        cache_len[b] = n
+    return k, v, cache_len, pad, err

@@ -241,3 +241,124 @@ def test_in_place_commit_order_is_safe():
                 got[0, 0, L + g0 + i] = r
         np.testing.assert_array_equal(got, want)
         assert all(path[j] >= j for j in range(tau)) and depth[end] + 1 == tau
+
+
+# ------------------------------------------------------------ compaction of pad slots
+
+def _golden_compact():
+    with open(os.path.join(os.path.dirname(__file__), "golden", "kv_compact.json")) as f:
+        return json.load(f)
+
+
+def _check_compact_golden(fn):
+    """True iff `fn` (a compaction with the oracle's signature) reproduces the
+    hand-enumerated fixture."""
+    g = _golden_compact()
+    B, cap = len(g["cache_len"]), g["capacity"]
+    slot = np.broadcast_to(np.arange(cap, dtype=np.float64)[None, None, :, None], (B, 2, cap, 4))
+    k2, v2, cl2, pad2, err = fn(slot, -slot, np.array(g["cache_len"]), np.array(g["pad"], np.uint8))
+    if err != 0 or list(cl2) != g["expected_cache_len"]:
+        return False
+    for b in range(B):
+        n, L = g["expected_cache_len"][b], g["cache_len"][b]
+        src = np.array(g["expected_slot_source"][b], dtype=np.float64)
+        if not (np.array_equal(k2[b, :, :n, :], np.broadcast_to(src[None, :, None], (2, n, 4))) and
+                np.array_equal(v2[b, :, :n, :], -k2[b, :, :n, :]) and not pad2[b, :L].any()):
+            return False
+    return True
+
+
+def test_compact_golden():
+    assert _check_compact_golden(oracle.compact_ref)
+
+
+def test_compact_planted_mistakes_fail_the_golden_case():
+    """Two plausible mistakes: a range that stops one slot short (the last
+    cached slot is never kept), and ignoring the pad bytes."""
+    def range_one_short(k, v, cache_len, pad):
+        return oracle.compact_ref(k, v, np.maximum(np.asarray(cache_len) - 1, 0), pad)
+
+    def keeps_pads(k, v, cache_len, pad):
+        return oracle.compact_ref(k, v, cache_len, np.zeros_like(pad))
+
+    assert not _check_compact_golden(range_one_short)
+    assert not _check_compact_golden(keeps_pads)
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_attention_over_compacted_cache_needs_no_mask(seed):
+    """After compaction, plain attention (no mask) over the first cache_len
+    slots equals attention over the padded cache with its pad slots masked;
+    the oracle's tree verify over the compacted cache without pads equals its
+    verify over the padded cache; the position remap is unchanged."""
+    rng = np.random.default_rng(7600 + seed)
+    B, Hq, Hkv, D, cap = 3, 4, 2, 16, 120
+    lens = rng.integers(0, cap + 1, size=B).astype(np.int32)
+    lens[0] = cap
+    pad = (rng.random((B, cap)) < 0.3).astype(np.uint8)
+    for b in range(B):
+        pad[b, lens[b]:] = rng.integers(0, 2, size=cap - lens[b])   # bytes past cache_len ignored
+    k = rng.standard_normal((B, Hkv, cap, D))
+    v = rng.standard_normal((B, Hkv, cap, D))
+    k2, v2, cl2, pad2, err = oracle.compact_ref(k, v, lens, pad)
+    assert err == 0
+    scale = 1 / math.sqrt(D)
+    G = Hq // Hkv
+    q = rng.standard_normal((B, Hq, D))
+    for b in range(B):
+        n = int(cl2[b])
+        assert n == int((pad[b, :lens[b]] == 0).sum())
+        assert not pad2[b, :lens[b]].any()
+        for g in range(Hkv):
+            if n == 0:
+                continue
+            masked = _sdpa_over_cache(q[b, g * G:(g + 1) * G], k[b, g], v[b, g], pad[b],
+                                      int(lens[b]), scale)
+            qt = torch.from_numpy(q[b, g * G:(g + 1) * G])[None, None]
+            plain = torch.nn.functional.scaled_dot_product_attention(
+                qt, torch.from_numpy(k2[b, g, :n])[None, None],
+                torch.from_numpy(v2[b, g, :n])[None, None], scale=scale)[0, 0].numpy()
+            np.testing.assert_allclose(plain, masked, rtol=0, atol=1e-12)
+    tree = synth.layered_tree(rng, (2, 3))
+    N = tree.n
+    tk = rng.standard_normal((B, Hkv, N, D))
+    tv = rng.standard_normal((B, Hkv, N, D))
+    qv = rng.standard_normal((B, N, Hq, D))
+    ref, lse = oracle.verify_attn_ref(qv, k, v, lens, tk, tv, tree.parents, scale=scale, pad=pad)
+    got, lse2 = oracle.verify_attn_ref(qv, k2, v2, cl2, tk, tv, tree.parents, scale=scale,
+                                       pad=np.zeros_like(pad))
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(oracle.position_ids(cl2, np.zeros_like(pad), tree.parents),
+                                  oracle.position_ids(lens, pad, tree.parents))
+
+
+def test_compact_is_idempotent_and_leaves_unpadded_caches_alone():
+    rng = np.random.default_rng(7700)
+    B, Hkv, D, cap = 4, 2, 8, 50
+    lens = np.array([50, 17, 0, 33], dtype=np.int32)
+    pad = (rng.random((B, cap)) < 0.2).astype(np.uint8)
+    pad[1] = 0
+    k = rng.standard_normal((B, Hkv, cap, D)).astype(np.float32)
+    v = rng.standard_normal((B, Hkv, cap, D)).astype(np.float32)
+    k1, v1, cl1, p1, e1 = oracle.compact_ref(k, v, lens, pad)
+    k2, v2, cl2, p2, e2 = oracle.compact_ref(k1, v1, cl1, p1)
+    assert e1 == e2 == 0
+    np.testing.assert_array_equal(cl1, cl2)
+    np.testing.assert_array_equal(k1, k2)
+    np.testing.assert_array_equal(v1, v2)
+    np.testing.assert_array_equal(k1[1], k[1])      # no pads: nothing moves
+    assert cl1[1] == 17 and cl1[2] == 0
+
+
+def test_compact_bad_cache_length_leaves_the_sequence_alone():
+    rng = np.random.default_rng(7800)
+    B, Hkv, D, cap = 3, 1, 4, 10
+    lens = np.array([11, -1, 6], dtype=np.int32)
+    pad = np.ones((B, cap), dtype=np.uint8)
+    k = rng.standard_normal((B, Hkv, cap, D))
+    k2, v2, cl2, pad2, err = oracle.compact_ref(k, k, lens, pad)
+    assert err == 1
+    np.testing.assert_array_equal(cl2, [11, -1, 0])
+    np.testing.assert_array_equal(k2[:2], k[:2])
+    np.testing.assert_array_equal(pad2[:2], pad[:2])
+    assert not pad2[2, :6].any() and pad2[2, 6:].all()
