@@ -16,6 +16,8 @@
  *                           the longest accepted root path and the bonus token.
  *   spec_kv_commit          append the accepted path's K/V to the cache,
  *                           padding the batch to one uniform length.
+ *   spec_kv_compact         drop a cache's padding slots (the valid slots
+ *                           move to the front, in order).
  *   spec_block_means,       budget selection: block summaries of the keys,
  *   spec_select_blocks      then a budget list of sink, best-scoring blocks
  *                           and window for the draft's budget mode.
@@ -287,6 +289,40 @@ spec_status spec_kv_commit(int32_t batch, int32_t n_kv_heads, int32_t head_dim, 
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Compaction of a cache's padding slots ([SM] Figure 9: batched commits pad
+ * every sequence to one length per step; [PV] section 3.3: tokens that were
+ * not accepted leave the cache once verification is done).  The maintenance
+ * step that removes the pads spec_kv_commit leaves behind.
+ *
+ * For every sequence b with 0 <= cache_len[b] <= capacity: the slots
+ * j < cache_len[b] whose pad byte is 0 keep their order and their K and V
+ * rows (every KV head) move to slots 0, 1, ..., n_b - 1; cache_len[b]
+ * becomes n_b; pad[b][j] becomes 0 for every j below the old cache_len.  The
+ * contents of the slots from n_b to the old cache_len are unspecified
+ * afterwards; slots and pad bytes at or past the old cache_len are not
+ * touched.  Attention over the compacted cache needs no mask, and the
+ * position of every token (spec_attn_verify_tree's pos_ids) is unchanged.
+ * A sequence with cache_len[b] outside [0, capacity] raises
+ * SPEC_DEV_CACHE_LEN and is left untouched.
+ *
+ * In place.  The time grows with the slots after a sequence's first pad
+ * (those rows move): pads near the end, as per-step commits leave them,
+ * keep it short; finding the first pad reads the pad bytes below cache_len.
+ *
+ * dtype SPEC_F32 or SPEC_BF16 (element size only: rows are copied);
+ * head_dim 64 or 128; the cache follows the spec_kv layout rules; cache_len
+ * int32 [B] (read and written); pad uint8 [B][pad_stride_b] (read and
+ * written), 4-byte aligned with pad_stride_b % 4 == 0 and >= capacity.
+ * batch = 0 launches nothing (pointers may be NULL).  Workspace:
+ * spec_compact_workspace_bytes(batch) bytes (the device error word and two
+ * int32 per sequence).
+ */
+spec_status spec_kv_compact(int32_t batch, int32_t n_kv_heads, int32_t head_dim, int32_t dtype,
+                            const spec_kv_mut* cache, int32_t* cache_len,
+                            uint8_t* pad, int64_t pad_stride_b,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Block summaries for budget selection ([PV] section 3.2: the partial cache
  * is chosen at the block level of the cache manager; section 4.1: mean
  * reduction for the retrieval).
@@ -400,6 +436,7 @@ size_t spec_verify_workspace_bytes(const spec_dims* dims, int32_t n_nodes,
                                    int32_t capacity);
 size_t spec_accept_workspace_bytes(int32_t batch, int32_t n_nodes, int32_t vocab);
 size_t spec_commit_workspace_bytes(void);
+size_t spec_compact_workspace_bytes(int32_t batch);
 size_t spec_select_workspace_bytes(const spec_dims* dims, int32_t max_blocks);
 
 /* Waits for `stream`, reads and clears the device error word of `workspace`.

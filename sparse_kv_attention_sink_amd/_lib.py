@@ -35,7 +35,7 @@ SPEC_VERIFY_PARTIAL = 1
 
 EXPORTED = [
     "spec_attn_draft_sparse", "spec_attn_draft_ring", "spec_attn_verify_tree",
-    "spec_accept_greedy", "spec_kv_commit",
+    "spec_accept_greedy", "spec_kv_commit", "spec_kv_compact", "spec_compact_workspace_bytes",
     "spec_draft_workspace_bytes", "spec_verify_workspace_bytes", "spec_accept_workspace_bytes",
     "spec_commit_workspace_bytes", "spec_block_means", "spec_select_blocks",
     "spec_select_workspace_bytes", "spec_kv_gather", "spec_verify_mode",
@@ -86,6 +86,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.spec_kv_commit.restype = I32
     lib.spec_commit_workspace_bytes.argtypes = []
     lib.spec_commit_workspace_bytes.restype = SZ
+    lib.spec_kv_compact.argtypes = [I32, I32, I32, I32, P, P, P, I64, P, SZ, P]
+    lib.spec_kv_compact.restype = I32
+    lib.spec_compact_workspace_bytes.argtypes = [I32]
+    lib.spec_compact_workspace_bytes.restype = SZ
     lib.spec_block_means.argtypes = [P, P, P, P, I64, I32, I32, I32, P, I32, P, SZ, P]
     lib.spec_block_means.restype = I32
     lib.spec_select_blocks.argtypes = [P, P, I32, P, I32, I32, P, I32, P, I64, I32, I32, I32, I32,
@@ -363,6 +367,31 @@ def spec_kv_commit(k_cache, v_cache, cache_len, pad, tree_k, tree_v, accept_len,
                             _ptr(n_appended), _ptr(workspace), workspace.numel(), _stream(k_cache))
     _check(st)
     return n_appended
+
+
+def compact_workspace_bytes(batch: int) -> int:
+    return int(load().spec_compact_workspace_bytes(batch))
+
+
+def spec_kv_compact(k_cache, v_cache, cache_len, pad, *, workspace=None):
+    """Drop each sequence's padding slots in place: the valid slots below
+    ``cache_len[b]`` move to the front in order, ``cache_len`` becomes their
+    count and the pad bytes below the old length are cleared."""
+    lib = load()
+    _on_gpu(k_cache, v_cache, cache_len, pad)
+    B, Hkv, _, D = k_cache.shape
+    if cache_len.dtype != torch.int32 or cache_len.numel() != B or not cache_len.is_contiguous():
+        raise ValueError("cache_len must be a contiguous int32 [B] tensor")
+    if pad.dtype != torch.uint8 or pad.dim() != 2 or pad.shape[0] != B or pad.stride(1) != 1 or \
+            pad.shape[1] < k_cache.shape[2]:
+        raise ValueError("pad must be uint8 [B, >= L_cap]")
+    kv = _kv(k_cache, v_cache)
+    if workspace is None:
+        workspace = new_workspace(compact_workspace_bytes(B), k_cache.device)
+    st = lib.spec_kv_compact(B, Hkv, D, _dtype_code(k_cache), ctypes.byref(kv), _ptr(cache_len),
+                             _ptr(pad), pad.stride(0), _ptr(workspace), workspace.numel(),
+                             _stream(k_cache))
+    _check(st)
 
 
 def select_workspace_bytes(dims: SpecDims, max_blocks: int = 0) -> int:

@@ -592,6 +592,54 @@ spec_status spec_kv_commit(int32_t batch, int32_t n_kv_heads, int32_t head_dim, 
 
 size_t spec_commit_workspace_bytes(void) { return kHeaderBytes; }
 
+// header | [B][2] int32: first pad slot and pad count per sequence
+size_t spec_compact_workspace_bytes(int32_t batch) {
+  return kHeaderBytes + align_up((size_t)std::max(batch, 0) * 2 * sizeof(int32_t), 256);
+}
+
+spec_status spec_kv_compact(int32_t batch, int32_t n_kv_heads, int32_t head_dim, int32_t dtype,
+                            const spec_kv_mut* cache, int32_t* cache_len, uint8_t* pad,
+                            int64_t pad_stride_b, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  const spec_dims d{batch, n_kv_heads, n_kv_heads, head_dim, dtype, 1.f};
+  spec_status st = check_dims(&d);
+  if (st != SPEC_OK) return st;
+  if ((int64_t)batch * n_kv_heads > INT32_MAX)
+    return fail(SPEC_E_UNSUPPORTED, "batch x n_kv_heads is too large");
+  if (batch == 0) return SPEC_OK;   // nothing to read or write; pointers may be NULL
+  if (cache == nullptr) return fail(SPEC_E_INVALID, "cache is NULL");
+  const spec_kv c{cache->k, cache->v, cache->stride_b, cache->stride_h, cache->stride_t, cache->capacity};
+  if ((st = check_kv(&c, &d, "cache", true)) != SPEC_OK) return st;
+  if (cache_len == nullptr || pad == nullptr) return fail(SPEC_E_INVALID, "a required pointer is NULL");
+  if (!aligned(cache_len, 4)) return fail(SPEC_E_INVALID, "cache_len must be 4-byte aligned");
+  if (!aligned(pad, 4) || pad_stride_b % 4 != 0 || pad_stride_b < cache->capacity)
+    return fail(SPEC_E_INVALID, "pad must be 4-byte aligned with pad_stride_b %% 4 == 0 and >= capacity");
+  const size_t need = spec_compact_workspace_bytes(batch);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(SPEC_E_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  if (!aligned(workspace, 256)) return fail(SPEC_E_INVALID, "workspace must be 256-byte aligned");
+  const int64_t es = esize(dtype);
+  CompactArgs a;
+  a.k = static_cast<char*>(cache->k);
+  a.v = static_cast<char*>(cache->v);
+  a.c_sb = cache->stride_b * es;
+  a.c_sh = cache->stride_h * es;
+  a.c_st = cache->stride_t * es;
+  a.batch = batch;
+  a.n_kv_heads = n_kv_heads;
+  a.row_chunks = (int32_t)(head_dim * es / 16);
+  a.capacity = cache->capacity;
+  a.cache_len = cache_len;
+  a.pad = pad;
+  a.pad_sb = pad_stride_b;
+  a.summary = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) + kHeaderBytes);
+  a.err = static_cast<uint32_t*>(workspace);
+  hipError_t e = launch_kv_compact(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "kv compact launch");
+  return SPEC_OK;
+}
+
 spec_status spec_block_means(const spec_dims* dims, const spec_kv* cache, const int32_t* cache_len,
                              const uint8_t* pad_or_null, int64_t pad_stride_b, int32_t block,
                              int32_t first_block, int32_t n_blocks, float* means,

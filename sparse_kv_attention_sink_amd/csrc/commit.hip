@@ -98,10 +98,176 @@ __global__ __launch_bounds__(256) void kv_commit_kernel(CommitArgs a) {
   if (tid == 0) a.cache_len[b] = L + P;
 }
 
+// ------------------------------------------------------------ compaction
+//
+// Dropping the pad slots that batched commits leave behind (SpecMemo review,
+// Figure 9; SpecPV section 3.3): the valid slots below cache_len keep their
+// order and move to the front, cache_len becomes their count and the pad
+// bytes below the old cache_len are cleared.
+//
+// kv_compact_move_kernel: one workgroup per (sequence, KV head), in place.
+// It first finds the sequence's first pad slot f and its pad count with
+// 16-byte scans of the pad bytes; slots below f stay where they are.  From f
+// on, chunks of 256 slots are handled in increasing order: a block prefix
+// sum of the chunk's pad bytes gives each valid slot j its destination
+// d(j) = j - (pads before j) <= j.  The rows of a chunk move in passes of
+// kCompactRows rows, each loading all its rows before storing any.  A store
+// lands at d(j) <= j, below every row a later pass or chunk reads, and on a
+// row of its own pass only after that pass's loads have completed; distinct
+// valid slots have distinct destinations.  So no row is overwritten before
+// it has been read.
+// kv_compact_finish_kernel: one workgroup per sequence, after the moves:
+// cache_len and the pad bytes.
+
+constexpr int kCompactChunk = 256;   // slots per prefix-sum chunk (one per thread)
+constexpr int kCompactItems = 8;     // 16-byte pieces each thread moves per pass
+
+__device__ __forceinline__ int nonzero_bytes(uint32_t w) {
+  return __popc(((w & 0x7f7f7f7fu) + 0x7f7f7f7fu | w) & 0x80808080u);
+}
+__device__ __forceinline__ int first_nonzero_byte(uint32_t w) {   // 4 if none
+  const uint32_t m = ((w & 0x7f7f7f7fu) + 0x7f7f7f7fu | w) & 0x80808080u;
+  return m ? (__ffs(m) - 1) >> 3 : 4;
+}
+
+__global__ __launch_bounds__(256) void kv_compact_move_kernel(CompactArgs a) {
+  const int b = blockIdx.x / a.n_kv_heads, h = blockIdx.x % a.n_kv_heads;
+  const int tid = threadIdx.x;
+  __shared__ int s_first[4], s_cnt[4];
+  __shared__ int dest_s[kCompactChunk];
+  __shared__ int scan_s[kCompactChunk];
+  const int L = a.cache_len[b];
+  if (L < 0 || L > a.capacity) {
+    if (h == 0 && tid == 0) raise_error(a.err, SPEC_DEV_CACHE_LEN);
+    return;
+  }
+  const uint8_t* prow = a.pad + (int64_t)b * a.pad_sb;
+
+  // ---- first pad slot and pad count over [0, L)
+  int first = INT_MAX, cnt = 0;
+  const int head = min(L, (int)((16 - (reinterpret_cast<uintptr_t>(prow) & 15)) & 15));
+  if (tid < head && prow[tid]) {
+    first = tid;
+    cnt = 1;
+  }
+  const int nvec = (L - head) / 16;
+  const uint4* pv = reinterpret_cast<const uint4*>(prow + head);
+  for (int i0 = 0; i0 < nvec; i0 += 256 * 8) {
+    uint4 w[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * 256 + tid;
+      w[u] = i < nvec ? pv[i] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int base = head + 16 * (i0 + u * 256 + tid);
+      const uint32_t q[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        cnt += nonzero_bytes(q[e]);
+        const int f = first_nonzero_byte(q[e]);
+        if (f < 4) first = min(first, base + 4 * e + f);
+      }
+    }
+  }
+  for (int j = head + 16 * nvec + tid; j < L; j += 256)
+    if (prow[j]) {
+      first = min(first, j);
+      ++cnt;
+    }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    first = min(first, __shfl_xor(first, m, 64));
+    cnt += __shfl_xor(cnt, m, 64);
+  }
+  if ((tid & 63) == 0) {
+    s_first[tid >> 6] = first;
+    s_cnt[tid >> 6] = cnt;
+  }
+  __syncthreads();
+  first = min(min(s_first[0], s_first[1]), min(s_first[2], s_first[3]));
+  cnt = s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
+  if (h == 0 && tid == 0) {
+    a.summary[2 * b] = first == INT_MAX ? L : first;
+    a.summary[2 * b + 1] = cnt;
+  }
+  if (first == INT_MAX) return;   // no pad: nothing moves
+
+  // ---- moves, chunk by chunk from the first pad
+  const int rc = a.row_chunks;
+  const int rows_per_pass = 256 * kCompactItems / rc;   // rc divides 256 * kCompactItems
+  char* const base_k = a.k + (int64_t)b * a.c_sb + (int64_t)h * a.c_sh;
+  char* const base_v = a.v + (int64_t)b * a.c_sb + (int64_t)h * a.c_sh;
+  int before = 0;   // pads in [first, c0)
+  for (int c0 = first; c0 < L; c0 += kCompactChunk) {
+    const int j = c0 + tid;
+    const int flag = j < L ? (prow[j] != 0) : 1;
+    // inclusive block scan of the flags (Hillis-Steele in LDS)
+    scan_s[tid] = flag;
+    __syncthreads();
+    for (int o = 1; o < kCompactChunk; o <<= 1) {
+      const int add = tid >= o ? scan_s[tid - o] : 0;
+      __syncthreads();
+      scan_s[tid] += add;
+      __syncthreads();
+    }
+    const int excl = scan_s[tid] - flag;
+    dest_s[tid] = flag ? -1 : j - (before + excl);
+    const int total = scan_s[kCompactChunk - 1];
+    __syncthreads();
+    before += total;
+    for (int tsr = 0; tsr < 2; ++tsr) {
+      char* const base = tsr ? base_v : base_k;
+      for (int r0 = 0; r0 < kCompactChunk; r0 += rows_per_pass) {
+        uint4 val[kCompactItems];
+        int dst[kCompactItems];
+#pragma unroll
+        for (int u = 0; u < kCompactItems; ++u) {
+          const int it = u * 256 + tid;
+          const int r = r0 + it / rc, ch = it % rc;
+          const int d = r < kCompactChunk ? dest_s[r] : -1;
+          dst[u] = d == c0 + r ? -1 : d;   // destination slot of a row that moves, else -1
+          if (dst[u] >= 0)
+            val[u] = *reinterpret_cast<const uint4*>(base + (int64_t)(c0 + r) * a.c_st + ch * 16);
+        }
+        wait_vm<0>();
+        __syncthreads();   // every load of this pass has returned
+#pragma unroll
+        for (int u = 0; u < kCompactItems; ++u) {
+          if (dst[u] < 0) continue;
+          const int ch = (u * 256 + tid) % rc;
+          *reinterpret_cast<uint4*>(base + (int64_t)dst[u] * a.c_st + ch * 16) = val[u];
+        }
+      }
+    }
+    __syncthreads();   // dest_s and scan_s are rewritten by the next chunk
+  }
+}
+
+__global__ __launch_bounds__(256) void kv_compact_finish_kernel(CompactArgs a) {
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int L = a.cache_len[b];
+  if (L < 0 || L > a.capacity) return;
+  const int first = a.summary[2 * b], cnt = a.summary[2 * b + 1];
+  uint8_t* prow = a.pad + (int64_t)b * a.pad_sb;
+  for (int j = first + tid; j < L; j += 256) prow[j] = 0;
+  __syncthreads();   // every thread has read cache_len[b]
+  if (tid == 0) a.cache_len[b] = L - cnt;
+}
+
 }  // namespace
 
 hipError_t launch_kv_commit(const CommitArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(kv_commit_kernel, dim3((unsigned)a.batch), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_compact(const CompactArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(kv_compact_move_kernel, dim3((unsigned)(a.batch * a.n_kv_heads)), dim3(256), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kv_compact_finish_kernel, dim3((unsigned)a.batch), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

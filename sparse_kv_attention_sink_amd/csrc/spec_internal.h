@@ -115,6 +115,19 @@ struct CommitArgs {
   uint32_t* err;
 };
 
+// Arguments of the compaction kernels (byte strides; validated by the caller).
+struct CompactArgs {
+  char* k;
+  char* v;
+  int64_t c_sb, c_sh, c_st;            // cache strides in bytes
+  int32_t batch, n_kv_heads, row_chunks, capacity;
+  int32_t* cache_len;
+  uint8_t* pad;
+  int64_t pad_sb;
+  int32_t* summary;                    // [B][2] in the workspace: first pad slot, pad count
+  uint32_t* err;
+};
+
 // Arguments of the block-mean kernel (byte strides; validated by the caller).
 struct MeansArgs {
   const char* k;
@@ -174,6 +187,7 @@ hipError_t launch_accept(int B, int N, int V, const float* logits, const int32_t
                          int32_t* accept_len, int32_t* accept_path, int32_t* bonus,
                          void* ws, int vsplits, hipStream_t st, uint32_t* err);
 hipError_t launch_kv_commit(const CommitArgs& a, hipStream_t st);
+hipError_t launch_kv_compact(const CompactArgs& a, hipStream_t st);
 hipError_t launch_block_means(const MeansArgs& a, hipStream_t st);
 hipError_t launch_select_blocks(const SelectArgs& a, hipStream_t st);
 hipError_t launch_kv_gather(const GatherArgs& a, hipStream_t st);
