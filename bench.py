@@ -510,6 +510,56 @@ def run_ragged(args, torch, skg):
     return out
 
 
+# ------------------------------------------------------------ compaction
+
+def run_compact(torch, skg, reps=20):
+    """Compaction of pad slots, in place, on the ragged batch of 16 (contexts
+    2K-32K with the tail pad pattern of the last 32 verify steps) and on the
+    1M-token sequence with the same tail pattern.  Every timed call starts
+    from the padded state again (cache_len and pad restored outside the timed
+    events; the rows it moves are the same each time)."""
+    import numpy as np
+    import synth
+    dev = torch.device("cuda:0")
+    out = {}
+    for name, B, cap, lens in (("ragged_batch16", 16, 32768, None), ("1m", 1, L1M, [L1M])):
+        rng = np.random.default_rng(synth.SEEDS[5] + 77)
+        lens = rng.integers(2048, cap + 1, size=B).astype(np.int32) if lens is None \
+            else np.asarray(lens, np.int32)
+        pad_np = np.zeros((B, cap), dtype=np.uint8)
+        for b in range(B):
+            pad_np[b, :lens[b]] = synth.pad_groups(rng, int(lens[b]))
+        k = torch.zeros((B, HKV, cap, D), dtype=torch.bfloat16, device=dev)
+        v = torch.zeros_like(k)
+        cl0 = torch.from_numpy(lens).to(dev)
+        pad0 = torch.from_numpy(pad_np).to(dev)
+        cl, pad = cl0.clone(), pad0.clone()
+        ws = skg.new_workspace(skg.compact_workspace_bytes(B), dev)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+        prerecord([e for p in ev for e in p], torch)
+        for i in range(reps + 2):
+            cl.copy_(cl0)
+            pad.copy_(pad0)
+            if i >= 2: ev[i - 2][0].record()
+            skg.spec_kv_compact(k, v, cl, pad, workspace=ws)
+            if i >= 2: ev[i - 2][1].record()
+        torch.cuda.synchronize()
+        assert skg.spec_device_status(ws) == 0
+        assert cl.cpu().numpy().tolist() == [int(lens[b] - pad_np[b, :lens[b]].sum()) for b in range(B)]
+        us = sum(a.elapsed_time(b) for a, b in ev) / reps * 1e3
+        moved = 0
+        for b in range(B):
+            row = pad_np[b, :lens[b]]
+            f = int(np.argmax(row)) if row.any() else int(lens[b])
+            moved += int((row[f:] == 0).sum())
+        out[name] = dict(batch=B, context_sum=int(lens.sum()), pad_slots=int(pad_np.sum()),
+                         rows_moved_per_head=moved, us_per_call=round(us, 2),
+                         bytes_moved=moved * HKV * 2 * D * ESZ * 2, pad_bytes_scanned=int(lens.sum()))
+        del k, v
+        torch.cuda.empty_cache()
+    return out
+
+
 # ------------------------------------------------------------ KV commit
 
 def run_commit(torch, skg, *, B, L, widths, depths, seed, reps=60):
@@ -948,6 +998,9 @@ def main():
     }
     log(f"[bench] kv commit: {commit['16k_batch8_tree64']['us_per_call']} us (16K batch 8), "
         f"{commit['1m_chain3']['us_per_call']} us (1M chain 3)")
+    compact = run_compact(torch, skg)
+    log(f"[bench] compaction: {compact['ragged_batch16']['us_per_call']} us (ragged batch 16), "
+        f"{compact['1m']['us_per_call']} us (1M)")
     select = run_select(torch, skg)
     log(f"[bench] block means table: {select['means_table_us']} us; selection: "
         + ", ".join(f"{k} {v['us_per_call']} us" for k, v in select["select"].items()))
@@ -988,6 +1041,7 @@ def main():
         "ctx4k": r4k,
         "ragged": rrag,
         "kv_commit": commit,
+        "kv_compact": compact,
         "budget_select": select,
         "partial_verify_1m": partial,
         "ring_draft_1m": ring,
