@@ -87,17 +87,14 @@ Plan bf16_plan(const spec_dims* d, int32_t T, int64_t tiles, bool gather, bool v
   const int G = d->n_q_heads / d->n_kv_heads;
   const int64_t pairs = (int64_t)d->batch * d->n_kv_heads;
   p.rows = T * G;
-  int64_t ring;
   if (p.rows <= 32) {           // few rows: four private rings per workgroup
     p.wk = 4;
     p.rt = (int32_t)cdiv(p.rows, 16);
     p.rb = 16 * p.rt;
-    ring = std::max<int64_t>(4 * 128 * d->head_dim, 4 * p.rb * (d->head_dim + 2) * 4);
   } else {                      // many rows: one shared ring, 4 x 16*rt rows
     p.wk = 1;
     p.rt = (int32_t)std::min<int64_t>(2, cdiv(p.rows, 64));
     p.rb = 64 * p.rt;
-    ring = (p.rt >= 3 ? 6 : 4) * 128 * d->head_dim;
   }
   p.n_rb = (int32_t)cdiv(p.rows, p.rb);
   if (tiles < 1) tiles = 1;

@@ -1006,7 +1006,7 @@ void attn_bf16_kernel(AttnArgs a) {
 
 template <int MODE, int D, int RT, int WK>
 static hipError_t launch_shape(const AttnArgs& a, hipStream_t st) {
-  constexpr int NS = WK == 1 ? (RT >= 3 ? 6 : 4) : 1;
+  constexpr int NS = WK == 1 ? 4 : 1;
   int64_t grid = a.units;
   if (a.n_rb > 1) grid = cdiv(a.units, 8) * 8 * a.n_rb;
   hipLaunchKernelGGL((attn_bf16_kernel<MODE, D, RT, WK, NS>), dim3((unsigned)grid), dim3(256), 0, st, a);
@@ -1019,12 +1019,8 @@ static hipError_t launch_mode(const AttnArgs& a, const Plan& p, hipStream_t st) 
     if (p.rt == 1) return launch_shape<MODE, D, 1, 4>(a, st);
     return launch_shape<MODE, D, 2, 4>(a, st);
   }
-  switch (p.rt) {
-    case 1: return launch_shape<MODE, D, 1, 1>(a, st);
-    case 2: return launch_shape<MODE, D, 2, 1>(a, st);
-    case 3: return launch_shape<MODE, D, 3, 1>(a, st);
-    default: return launch_shape<MODE, D, 4, 1>(a, st);
-  }
+  if (p.rt == 1) return launch_shape<MODE, D, 1, 1>(a, st);
+  return launch_shape<MODE, D, 2, 1>(a, st);   // (the plan uses at most two 16-row tiles)
 }
 
 hipError_t launch_attn_bf16(const AttnArgs& a, int mode, const Plan& p, hipStream_t st) {
