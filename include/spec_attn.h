@@ -307,14 +307,15 @@ spec_status spec_kv_commit(int32_t batch, int32_t n_kv_heads, int32_t head_dim, 
  *
  * In place.  The time grows with the slots after a sequence's first pad
  * (those rows move): pads near the end, as per-step commits leave them,
- * keep it short; finding the first pad reads the pad bytes below cache_len.
+ * keep it short.  Finding the first pad reads the pad bytes below cache_len
+ * once, in 64 slices per sequence.
  *
  * dtype SPEC_F32 or SPEC_BF16 (element size only: rows are copied);
  * head_dim 64 or 128; the cache follows the spec_kv layout rules; cache_len
  * int32 [B] (read and written); pad uint8 [B][pad_stride_b] (read and
  * written), 4-byte aligned with pad_stride_b % 4 == 0 and >= capacity.
  * batch = 0 launches nothing (pointers may be NULL).  Workspace:
- * spec_compact_workspace_bytes(batch) bytes (the device error word and two
+ * spec_compact_workspace_bytes(batch) bytes (the device error word and 128
  * int32 per sequence).
  */
 spec_status spec_kv_compact(int32_t batch, int32_t n_kv_heads, int32_t head_dim, int32_t dtype,

@@ -594,9 +594,9 @@ spec_status spec_kv_commit(int32_t batch, int32_t n_kv_heads, int32_t head_dim, 
 
 size_t spec_commit_workspace_bytes(void) { return kHeaderBytes; }
 
-// header | [B][2] int32: first pad slot and pad count per sequence
+// header | [B][kCompactSlices][2] int32: first pad slot and pad count per slice of the pad bytes
 size_t spec_compact_workspace_bytes(int32_t batch) {
-  return kHeaderBytes + align_up((size_t)std::max(batch, 0) * 2 * sizeof(int32_t), 256);
+  return kHeaderBytes + align_up((size_t)std::max(batch, 0) * kCompactSlices * 2 * sizeof(int32_t), 256);
 }
 
 spec_status spec_kv_compact(int32_t batch, int32_t n_kv_heads, int32_t head_dim, int32_t dtype,
@@ -606,7 +606,7 @@ spec_status spec_kv_compact(int32_t batch, int32_t n_kv_heads, int32_t head_dim,
   const spec_dims d{batch, n_kv_heads, n_kv_heads, head_dim, dtype, 1.f};
   spec_status st = check_dims(&d);
   if (st != SPEC_OK) return st;
-  if ((int64_t)batch * n_kv_heads > INT32_MAX)
+  if ((int64_t)batch * std::max(n_kv_heads, kCompactSlices) > INT32_MAX)
     return fail(SPEC_E_UNSUPPORTED, "batch x n_kv_heads is too large");
   if (batch == 0) return SPEC_OK;   // nothing to read or write; pointers may be NULL
   if (cache == nullptr) return fail(SPEC_E_INVALID, "cache is NULL");
@@ -636,6 +636,7 @@ spec_status spec_kv_compact(int32_t batch, int32_t n_kv_heads, int32_t head_dim,
   a.pad = pad;
   a.pad_sb = pad_stride_b;
   a.summary = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) + kHeaderBytes);
+  a.sliced = cache->capacity > kCompactScanSlots ? 1 : 0;
   a.err = static_cast<uint32_t*>(workspace);
   hipError_t e = launch_kv_compact(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "kv compact launch");

@@ -105,9 +105,14 @@ __global__ __launch_bounds__(256) void kv_commit_kernel(CommitArgs a) {
 // order and move to the front, cache_len becomes their count and the pad
 // bytes below the old cache_len are cleared.
 //
+// kv_compact_scan_kernel (capacities above kCompactScanSlots only):
+// kCompactSlices workgroups per sequence, each scanning one slice of the pad
+// bytes below cache_len with 16-byte loads for the slice's first pad slot
+// and pad count.  A shorter pad row is scanned by the move kernel itself,
+// which saves a launch.
 // kv_compact_move_kernel: one workgroup per (sequence, KV head), in place.
-// It first finds the sequence's first pad slot f and its pad count with
-// 16-byte scans of the pad bytes; slots below f stay where they are.  From f
+// It finds the sequence's first pad slot f and pad count (from the slices'
+// summaries, or by its own scan); slots below f stay where they are.  From f
 // on, chunks of 256 slots are handled in increasing order: a block prefix
 // sum of the chunk's pad bytes gives each valid slot j its destination
 // d(j) = j - (pads before j) <= j.  The rows of a chunk move in passes of
@@ -130,28 +135,21 @@ __device__ __forceinline__ int first_nonzero_byte(uint32_t w) {   // 4 if none
   return m ? (__ffs(m) - 1) >> 3 : 4;
 }
 
-__global__ __launch_bounds__(256) void kv_compact_move_kernel(CompactArgs a) {
-  const int b = blockIdx.x / a.n_kv_heads, h = blockIdx.x % a.n_kv_heads;
-  const int tid = threadIdx.x;
+// First pad slot (INT_MAX if none) and pad count of pad bytes [lo, hi) of
+// `prow`, reduced over the workgroup; every thread gets the result.
+__device__ void scan_pads(const uint8_t* prow, int lo, int hi, int& first_out, int& cnt_out) {
   __shared__ int s_first[4], s_cnt[4];
-  __shared__ int dest_s[kCompactChunk];
-  __shared__ int scan_s[kCompactChunk];
-  const int L = a.cache_len[b];
-  if (L < 0 || L > a.capacity) {
-    if (h == 0 && tid == 0) raise_error(a.err, SPEC_DEV_CACHE_LEN);
-    return;
-  }
-  const uint8_t* prow = a.pad + (int64_t)b * a.pad_sb;
-
-  // ---- first pad slot and pad count over [0, L)
+  const int tid = threadIdx.x;
   int first = INT_MAX, cnt = 0;
-  const int head = min(L, (int)((16 - (reinterpret_cast<uintptr_t>(prow) & 15)) & 15));
-  if (tid < head && prow[tid]) {
-    first = tid;
+  const int n = max(hi - lo, 0);
+  const uint8_t* p = prow + lo;
+  const int head = min(n, (int)((16 - (reinterpret_cast<uintptr_t>(p) & 15)) & 15));
+  if (tid < head && p[tid]) {
+    first = lo + tid;
     cnt = 1;
   }
-  const int nvec = (L - head) / 16;
-  const uint4* pv = reinterpret_cast<const uint4*>(prow + head);
+  const int nvec = (n - head) / 16;
+  const uint4* pv = reinterpret_cast<const uint4*>(p + head);
   for (int i0 = 0; i0 < nvec; i0 += 256 * 8) {
     uint4 w[8];
 #pragma unroll
@@ -161,7 +159,7 @@ __global__ __launch_bounds__(256) void kv_compact_move_kernel(CompactArgs a) {
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int base = head + 16 * (i0 + u * 256 + tid);
+      const int base = lo + head + 16 * (i0 + u * 256 + tid);
       const uint32_t q[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -171,9 +169,9 @@ __global__ __launch_bounds__(256) void kv_compact_move_kernel(CompactArgs a) {
       }
     }
   }
-  for (int j = head + 16 * nvec + tid; j < L; j += 256)
-    if (prow[j]) {
-      first = min(first, j);
+  for (int j = head + 16 * nvec + tid; j < n; j += 256)
+    if (p[j]) {
+      first = min(first, lo + j);
       ++cnt;
     }
 #pragma unroll
@@ -186,11 +184,69 @@ __global__ __launch_bounds__(256) void kv_compact_move_kernel(CompactArgs a) {
     s_cnt[tid >> 6] = cnt;
   }
   __syncthreads();
-  first = min(min(s_first[0], s_first[1]), min(s_first[2], s_first[3]));
-  cnt = s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
-  if (h == 0 && tid == 0) {
-    a.summary[2 * b] = first == INT_MAX ? L : first;
-    a.summary[2 * b + 1] = cnt;
+  first_out = min(min(s_first[0], s_first[1]), min(s_first[2], s_first[3]));
+  cnt_out = s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
+}
+
+// The sequence's first pad slot (INT_MAX if none) and pad count from its
+// slices' summaries; every thread gets the result.
+__device__ void combine_slices(const int32_t* sum_b, int& first_out, int& cnt_out) {
+  __shared__ int s_first, s_cnt;
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    int first = tid < kCompactSlices ? sum_b[2 * tid] : INT_MAX;
+    int cnt = tid < kCompactSlices ? sum_b[2 * tid + 1] : 0;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      first = min(first, __shfl_xor(first, m, 64));
+      cnt += __shfl_xor(cnt, m, 64);
+    }
+    if (tid == 0) {
+      s_first = first;
+      s_cnt = cnt;
+    }
+  }
+  __syncthreads();
+  first_out = s_first;
+  cnt_out = s_cnt;
+}
+
+__global__ __launch_bounds__(256) void kv_compact_scan_kernel(CompactArgs a) {
+  const int b = blockIdx.x / kCompactSlices, sl = blockIdx.x % kCompactSlices;
+  const int L = a.cache_len[b];
+  if (L < 0 || L > a.capacity) return;   // (the move kernel reports it)
+  const int per = (L + kCompactSlices - 1) / kCompactSlices;
+  const int lo = min(L, sl * per), hi = min(L, lo + per);
+  int first, cnt;
+  scan_pads(a.pad + (int64_t)b * a.pad_sb, lo, hi, first, cnt);
+  if (threadIdx.x == 0) {
+    a.summary[(b * kCompactSlices + sl) * 2] = first;
+    a.summary[(b * kCompactSlices + sl) * 2 + 1] = cnt;
+  }
+}
+
+__global__ __launch_bounds__(256) void kv_compact_move_kernel(CompactArgs a) {
+  const int b = blockIdx.x / a.n_kv_heads, h = blockIdx.x % a.n_kv_heads;
+  const int tid = threadIdx.x;
+  __shared__ int dest_s[kCompactChunk];
+  __shared__ int scan_s[kCompactChunk];
+  const int L = a.cache_len[b];
+  if (L < 0 || L > a.capacity) {
+    if (h == 0 && tid == 0) raise_error(a.err, SPEC_DEV_CACHE_LEN);
+    return;
+  }
+  const uint8_t* prow = a.pad + (int64_t)b * a.pad_sb;
+  int32_t* const sum_b = a.summary + (int64_t)b * kCompactSlices * 2;
+  int first, cnt;
+  if (a.sliced) {
+    combine_slices(sum_b, first, cnt);
+  } else {
+    scan_pads(prow, 0, L, first, cnt);
+    // the finish kernel reads slice summaries: the whole row as slice 0
+    if (h == 0 && tid < kCompactSlices) {
+      sum_b[2 * tid] = tid == 0 ? first : INT_MAX;
+      sum_b[2 * tid + 1] = tid == 0 ? cnt : 0;
+    }
   }
   if (first == INT_MAX) return;   // no pad: nothing moves
 
@@ -249,9 +305,10 @@ __global__ __launch_bounds__(256) void kv_compact_finish_kernel(CompactArgs a) {
   const int b = blockIdx.x, tid = threadIdx.x;
   const int L = a.cache_len[b];
   if (L < 0 || L > a.capacity) return;
-  const int first = a.summary[2 * b], cnt = a.summary[2 * b + 1];
+  int first, cnt;
+  combine_slices(a.summary + (int64_t)b * kCompactSlices * 2, first, cnt);
   uint8_t* prow = a.pad + (int64_t)b * a.pad_sb;
-  for (int j = first + tid; j < L; j += 256) prow[j] = 0;
+  for (int j = first == INT_MAX ? L : first + tid; j < L; j += 256) prow[j] = 0;
   __syncthreads();   // every thread has read cache_len[b]
   if (tid == 0) a.cache_len[b] = L - cnt;
 }
@@ -264,6 +321,11 @@ hipError_t launch_kv_commit(const CommitArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_kv_compact(const CompactArgs& a, hipStream_t st) {
+  if (a.sliced) {
+    hipLaunchKernelGGL(kv_compact_scan_kernel, dim3((unsigned)(a.batch * kCompactSlices)), dim3(256), 0, st, a);
+    hipError_t e0 = hipGetLastError();
+    if (e0 != hipSuccess) return e0;
+  }
   hipLaunchKernelGGL(kv_compact_move_kernel, dim3((unsigned)(a.batch * a.n_kv_heads)), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -30,6 +30,8 @@ constexpr int kMaxPadWords = 1024;             // 32-key pad words one workgroup
 constexpr int kMergeFan = 16;                  // partials one split-merge step reads
 constexpr int kMaxSplits = kMergeFan * kMergeFan;
 constexpr int kChunkTiles = 8;                 // tiles per dynamically taken chunk
+constexpr int kCompactSlices = 64;             // pad-scan workgroups per sequence (compaction)
+constexpr int kCompactScanSlots = 65536;       // compaction: longer pad rows are scanned in slices
 constexpr int kMaxSelectBlocks = 8192;         // candidate blocks one selection scores
 constexpr int kMaxSelect = 2048;               // blocks one selection may choose
 
@@ -120,11 +122,11 @@ struct CompactArgs {
   char* k;
   char* v;
   int64_t c_sb, c_sh, c_st;            // cache strides in bytes
-  int32_t batch, n_kv_heads, row_chunks, capacity;
+  int32_t batch, n_kv_heads, row_chunks, capacity, sliced;
   int32_t* cache_len;
   uint8_t* pad;
   int64_t pad_sb;
-  int32_t* summary;                    // [B][2] in the workspace: first pad slot, pad count
+  int32_t* summary;                    // [B][kCompactSlices][2] in the workspace: each slice's first pad slot, pad count
   uint32_t* err;
 };
 

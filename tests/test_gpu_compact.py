@@ -209,3 +209,23 @@ def test_ragged_workload_at_full_size():
         np.testing.assert_array_equal(gk[b][:, sl], k0[b][:, keep[sl]])
         np.testing.assert_array_equal(gv[b][:, sl], v0[b][:, keep[sl]])
         np.testing.assert_array_equal(gk[b][:, :max(0, f - 8)], k0[b][:, :max(0, f - 8)])
+
+
+def test_long_pad_rows_are_scanned_in_slices():
+    """Capacities above 64 Ki slots scan the pad bytes in 64 slices per
+    sequence (a launch of its own); lengths that do not divide evenly, pads
+    in the first slice, in a middle one and at the tail, and a sequence with
+    no pad."""
+    rng = np.random.default_rng(8900)
+    B, Hkv, D, cap = 3, 2, 64, 131084
+    lens = np.array([131084, 100003, 70001], dtype=np.int32)
+    k = synth.draw_normal(rng, (B, Hkv, cap, D), 1.0, "bf16")
+    v = synth.draw_normal(rng, (B, Hkv, cap, D), 1.0, "bf16")
+    pad = np.zeros((B, cap), dtype=np.uint8)
+    pad[0] = (rng.random(cap) < 0.01).astype(np.uint8)
+    pad[1, 70000] = 1
+    pad[1, 100003 - 100:100003] = (rng.random(100) < 0.5).astype(np.uint8)
+    pad[1, 100003:] = 1                      # past cache_len: ignored
+    got = run_compact(to_dev(k, "bf16"), to_dev(v, "bf16"), lens, pad)
+    check(k, v, lens, pad, got)
+    assert got[2][2] == 70001
