@@ -116,7 +116,8 @@ __global__ __launch_bounds__(256) void kv_commit_kernel(CommitArgs a) {
 // on, chunks of 256 slots are handled in increasing order: a block prefix
 // sum of the chunk's pad bytes gives each valid slot j its destination
 // d(j) = j - (pads before j) <= j.  The rows of a chunk move in passes of
-// kCompactRows rows, each loading all its rows before storing any.  A store
+// 64 to 256 rows (kCompactItems 16-byte pieces per thread), each loading all
+// its rows before storing any.  A store
 // lands at d(j) <= j, below every row a later pass or chunk reads, and on a
 // row of its own pass only after that pass's loads have completed; distinct
 // valid slots have distinct destinations.  So no row is overwritten before
