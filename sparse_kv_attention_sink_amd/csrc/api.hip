@@ -113,6 +113,14 @@ Plan bf16_plan(const spec_dims* d, int32_t T, int64_t tiles, bool gather, bool v
   // than the cross-workgroup merge a second split brings (a budget of 256 of
   // the 16K batch of 8: 10.2 -> 8.0 us per call, device time).
   if (p.wk == 4 && !verify && tiles <= 16) S = 1;
+  // A tree verify runs its splits longest sequence first, and the splits
+  // past a sequence's own length exit at once; so that a ragged batch's long
+  // sequences are spread over many workgroups, no split covers more than
+  // kOrderTiles tiles of the capacity.
+  if (verify && p.wk == 1 && d->batch <= kMaxOrderBatch) {
+    p.ordered = 1;
+    S = std::max(S, cdiv(tiles, kOrderTiles));
+  }
   S = std::min<int64_t>(std::max(S, lo), kMaxSplits);
   if (S < lo) {
     p.total = 0;
@@ -250,6 +258,7 @@ void fill_plan(AttnArgs& a, const Plan& p, void* workspace) {
   a.cnt_pos = a.cnt_l1 + groups;
   a.cnt_chunk = a.cnt_pos + 2 * (size_t)a.B;
   a.dyn = p.dyn;
+  a.ordered = p.ordered;
   a.err = reinterpret_cast<uint32_t*>(ws);
 }
 

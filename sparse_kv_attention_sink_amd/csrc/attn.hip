@@ -360,7 +360,31 @@ void attn_bf16_kernel(AttnArgs a) {
     z = slot % a.n_rb;
     if (unit >= a.units) return;
   }
-  const int s = unit % a.splits, pair = unit / a.splits;
+  int s = unit % a.splits, pair = unit / a.splits;
+  if constexpr (MODE == kVerify && WK == 1) {
+    if (a.ordered) {
+      // Splits in order of split index, and within one index the sequences
+      // longest first (ties: smaller index), so that the hardware starts the
+      // longest work first; a split past its sequence's length exits below.
+      __shared__ int32_t len_s[kMaxOrderBatch], ord_s[kMaxOrderBatch];
+      for (int i = threadIdx.x; i < a.B; i += 256) {
+        const int l = a.cache_len[i];
+        len_s[i] = (l >= 0 && l <= a.capacity) ? l : 0;
+      }
+      __syncthreads();
+      for (int i = threadIdx.x; i < a.B; i += 256) {
+        const int li = len_s[i];
+        int r = 0;
+        for (int j = 0; j < a.B; ++j) r += (len_s[j] > li) || (len_s[j] == li && j < i);
+        ord_s[r] = i;
+      }
+      __syncthreads();
+      const int pairs = a.B * a.Hkv;
+      s = unit / pairs;
+      const int k = unit % pairs;
+      pair = ord_s[k / a.Hkv] * a.Hkv + k % a.Hkv;
+    }
+  }
   const int b = pair / a.Hkv, g = pair % a.Hkv;
   // (the wave index is uniform within a wavefront; saying so keeps
   // everything derived from it, such as a wavefront's tile range and its
@@ -376,6 +400,18 @@ void attn_bf16_kernel(AttnArgs a) {
   bool bad = MODE == kVerify ? (L < 0 || L > a.capacity)
                              : (L < T || (a.kv_ring == 0 && L > a.capacity));   // a ring keeps the logical length
   if (leader && tid == 0 && bad) raise_error(a.err, SPEC_DEV_CACHE_LEN);
+  // Splits of this (sequence, KV head) that hold work: all of them, or, in
+  // the ordered verify, those that start below the sequence's own key count
+  // (a sequence with a bad length keeps one, which writes its poisoned rows).
+  int S_own = a.splits;
+  if constexpr (MODE == kVerify && WK == 1) {
+    if (a.ordered) {
+      const int Lv = bad ? 0 : L;
+      const int keys_tiles = (Lv + kTileKeys - 1) / kTileKeys + (N + kTileKeys - 1) / kTileKeys;
+      S_own = max(1, min(a.splits, (keys_tiles + a.tps - 1) / a.tps));
+      if (s >= S_own) return;
+    }
+  }
 
   // ---------------------------------------------------------------- tree
   if constexpr (MODE == kVerify) {
@@ -845,7 +881,7 @@ void attn_bf16_kernel(AttnArgs a) {
         uint32_t* cnt = a.cnt_pos + 2 * b;
         if (tid == 0 && pad_count)
           __hip_atomic_fetch_add(cnt + 1, (uint32_t)pad_count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        write = arrive_last(cnt, a.splits);
+        write = arrive_last(cnt, S_own);
         if (write && tid == 0)
           red_s[0] = (int)__hip_atomic_exchange(cnt + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __syncthreads();
@@ -863,7 +899,8 @@ void attn_bf16_kernel(AttnArgs a) {
     lr[rt] += shfl_xor(lr[rt], 16);
     lr[rt] += shfl_xor(lr[rt], 32);
   }
-  const int S = a.splits;
+  const int S = a.splits;   // the partial buffers' split dimension
+  const int So = S_own;      // splits of this pair that write a partial
   const size_t grp = (size_t)pair * a.n_rb + z;
   // this group's partials: o [S][RC][D], lse [S][RC] (log2 domain)
   const __amdgpu_buffer_rsrc_t o_rs = coherent_rsrc(a.o_part + grp * S * RC * D, (uint32_t)(S * RC * D * 4));
@@ -877,7 +914,7 @@ void attn_bf16_kernel(AttnArgs a) {
                        __attribute__((always_inline)) {
     const int row = z * RC + row_l;
     if (row >= R) return;
-    if (S > 1) {
+    if (So > 1) {
       store_sc1_f4(o_rs, (uint32_t)(((s * RC + row_l) * D + d0) * 4), f32x4{vals[0], vals[1], vals[2], vals[3]});
       if (lse_lane) store_sc1_f1(l_rs, (uint32_t)((s * RC + row_l) * 4), lse2);
       return;
@@ -963,15 +1000,15 @@ void attn_bf16_kernel(AttnArgs a) {
       store_row(rl, d0, o, d0 == 0, lse2);
     }
   }
-  if (S == 1) return;
+  if (So == 1) return;
 
   // ---------------------------------------------------------------- split merge
   // Two levels: the last of each block of up to kMergeFan splits merges the
   // block; with more than one block, the last block merger merges the block
   // results.  Every merge reads at most kMergeFan partials.
   const int rows = min(RC, a.R - z * RC);
-  const int nb = a.n_blk;
-  const int blk = s / kMergeFan, bsz = min(kMergeFan, S - blk * kMergeFan);
+  const int nb = (So + kMergeFan - 1) / kMergeFan;   // merge blocks of this pair
+  const int blk = s / kMergeFan, bsz = min(kMergeFan, So - blk * kMergeFan);
   auto final_sink = [&](int rl, int d0, const float* o, float lse2) __attribute__((always_inline)) {
     const int row = z * RC + rl;
     const int t = row / G, hh = row % G;
@@ -979,7 +1016,7 @@ void attn_bf16_kernel(AttnArgs a) {
     *reinterpret_cast<uint2*>(out + oi * D + d0) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
     if (d0 == 0 && lse_out != nullptr) lse_out[oi] = lse2 * kLn2;
   };
-  if (!arrive_last(a.cnt_l0 + grp * nb + blk, bsz)) return;
+  if (!arrive_last(a.cnt_l0 + grp * a.n_blk + blk, bsz)) return;
   // The (pair, row block)'s final merger: every split has arrived, so no
   // wave grabs chunks any more and the chunk counter can start over.
   auto reset_chunks = [&]() __attribute__((always_inline)) {
@@ -987,11 +1024,11 @@ void attn_bf16_kernel(AttnArgs a) {
   };
   if (nb == 1) {
     reset_chunks();
-    merge_partials<D, RC>(o_rs, l_rs, 0, S, rows, final_sink);
+    merge_partials<D, RC>(o_rs, l_rs, 0, So, rows, final_sink);
     return;
   }
-  const __amdgpu_buffer_rsrc_t o1_rs = coherent_rsrc(a.o_part1 + grp * nb * RC * D, (uint32_t)(nb * RC * D * 4));
-  const __amdgpu_buffer_rsrc_t l1_rs = coherent_rsrc(a.lse_part1 + grp * nb * RC, (uint32_t)(nb * RC * 4));
+  const __amdgpu_buffer_rsrc_t o1_rs = coherent_rsrc(a.o_part1 + grp * a.n_blk * RC * D, (uint32_t)(a.n_blk * RC * D * 4));
+  const __amdgpu_buffer_rsrc_t l1_rs = coherent_rsrc(a.lse_part1 + grp * a.n_blk * RC, (uint32_t)(a.n_blk * RC * 4));
   merge_partials<D, RC>(o_rs, l_rs, blk * kMergeFan, bsz, rows,
                         [&](int rl, int d0, const float* o, float lse2) __attribute__((always_inline)) {
                           store_sc1_f4(o1_rs, (uint32_t)(((blk * RC + rl) * D + d0) * 4), f32x4{o[0], o[1], o[2], o[3]});

@@ -30,6 +30,8 @@ constexpr int kMaxPadWords = 1024;             // 32-key pad words one workgroup
 constexpr int kMergeFan = 16;                  // partials one split-merge step reads
 constexpr int kMaxSplits = kMergeFan * kMergeFan;
 constexpr int kChunkTiles = 8;                 // tiles per dynamically taken chunk
+constexpr int kMaxOrderBatch = 256;            // tree verify: longest-first work order up to this batch
+constexpr int kOrderTiles = 384;               // tree verify (ordered): at most this many tiles per split
 constexpr int kCompactSlices = 64;             // pad-scan workgroups per sequence (compaction)
 constexpr int kCompactScanSlots = 65536;       // compaction: longer pad rows are scanned in slices
 constexpr int kMaxSelectBlocks = 8192;         // candidate blocks one selection scores
@@ -82,6 +84,7 @@ struct AttnArgs {
   uint32_t* cnt_pos;      // [B][2] pad-count arrival (verify positions)
   uint32_t* cnt_chunk;    // bf16 path: [pair][n_rb] next tile chunk (dynamic splits)
   int32_t dyn;            // bf16 path: tiles per dynamically taken chunk, 0 = fixed ranges
+  int32_t ordered;        // bf16 tree verify: splits in longest-sequence-first order, empty ones exit
   void* out;              // final output
   float* lse;             // final lse (natural log) or null
   uint32_t* err;          // device error word
@@ -94,6 +97,7 @@ struct Plan {
          total = 0;
   int32_t n_blk = 1;
   int32_t dyn = 0;          // tiles per dynamically taken chunk (0: fixed split ranges)
+  int32_t ordered = 0;      // tree verify in longest-first order (see AttnArgs)
 };
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
