@@ -223,3 +223,52 @@ def test_ragged_verify(shape, widths):
     assert_close(got, ref, dt, "ragged verify")
     assert_lse_close(lse, lse_ref, 1e-3 if dt == "bf16" else 1e-5, "ragged verify lse")
     np.testing.assert_array_equal(pos, oracle.position_ids(case.cache_len, pad, tree.parents))
+
+
+# ------------------------------------------------------------ tree-verify work order
+
+def test_verify_longest_first_with_empty_splits_and_two_merge_levels():
+    """A large capacity with sequences of very different lengths: in the
+    longest-first order the short sequence keeps one split (its output is
+    written directly), the middle one a few (one merge level) and the long
+    one twenty (two merge levels); the splits past each sequence's length
+    exit at once.  Pads in every sequence."""
+    B, Hq, Hkv, D, cap = 3, 8, 2, 128, 20000
+    lens = [20000, 100, 5000]
+    rng = np.random.default_rng(9300)
+    tree = synth.layered_tree(rng, (10, 14, 12, 8))
+    N = tree.n
+    case = synth.make_attn_case(9301, B=B, Hq=Hq, Hkv=Hkv, D=D, L_cap=cap, T=N, cache_len=lens,
+                                dtype="bf16", value_scale=1.0)
+    tk = synth.draw_normal(rng, (B, Hkv, N, D), 1.0, "bf16")
+    tv = synth.draw_normal(rng, (B, Hkv, N, D), 1.0, "bf16")
+    pad = np.zeros((B, cap), dtype=np.uint8)
+    for b in range(B):
+        pad[b, :lens[b]] = synth.pad_groups(rng, lens[b], n_groups=10, group=5)
+    got, lse, pos = run_verify(case, case.q, tk, tv, tree.parents, pad=pad)
+    ref, lse_ref = oracle.verify_attn_ref(case.q, case.k, case.v, case.cache_len, tk, tv,
+                                          tree.parents, scale=case.scale, pad=pad)
+    assert_close(got, ref, "bf16", "ordered verify")
+    assert_lse_close(lse, lse_ref, 1e-3, "ordered verify lse")
+    np.testing.assert_array_equal(pos, oracle.position_ids(case.cache_len, pad, tree.parents))
+
+
+def test_verify_batch_above_the_ordered_limit():
+    """A batch of 300 (above the 256 that the longest-first order ranks)
+    runs the tree verify in the plain split order."""
+    B, Hq, Hkv, D, cap = 300, 8, 2, 64, 96
+    rng = np.random.default_rng(9400)
+    lens = rng.integers(1, cap + 1, size=B).astype(np.int32)
+    tree = synth.layered_tree(rng, (3, 4, 3))
+    N = tree.n
+    case = synth.make_attn_case(9401, B=B, Hq=Hq, Hkv=Hkv, D=D, L_cap=cap, T=N, cache_len=lens,
+                                dtype="bf16", value_scale=1.0)
+    tk = synth.draw_normal(rng, (B, Hkv, N, D), 1.0, "bf16")
+    tv = synth.draw_normal(rng, (B, Hkv, N, D), 1.0, "bf16")
+    got, lse, pos = run_verify(case, case.q, tk, tv, tree.parents)
+    ref, lse_ref = oracle.verify_attn_ref(case.q, case.k, case.v, case.cache_len, tk, tv,
+                                          tree.parents, scale=case.scale)
+    # (unscaled values over contexts as short as one key: outputs reach about
+    # 3.5, where bf16 rounding alone is |x| 2^-8, so the bar scales with them)
+    assert_close(got, ref, "bf16", "verify batch 300", magnitude=max(1.0, float(np.nanmax(np.abs(ref)))))
+    np.testing.assert_array_equal(pos, oracle.position_ids(case.cache_len, None, tree.parents))
