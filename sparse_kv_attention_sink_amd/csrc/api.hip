@@ -89,7 +89,13 @@ Plan bf16_plan(const spec_dims* d, int32_t T, int64_t tiles, bool gather, bool v
   p.rows = T * G;
   if (p.rows <= 32) {           // few rows: four private rings per workgroup
     p.wk = 4;
-    p.rt = (int32_t)cdiv(p.rows, 16);
+    // Up to 32 rows fit one row block (two 16-row tiles per wavefront, one
+    // workgroup per CU by registers).  With few (sequence, KV head) pairs the
+    // grid is small, and two 16-row blocks, two workgroups per CU, finish
+    // sooner (the 4K chain of 5: 19.7 -> 17.1 us); with many pairs, the second
+    // block's reads of the same tiles cost more (the 16K batch-8 chain of 5:
+    // 112 -> 142 us).
+    p.rt = (pairs <= 16) ? 1 : (int32_t)cdiv(p.rows, 16);
     p.rb = 16 * p.rt;
   } else {                      // many rows: one shared ring, 4 x 16*rt rows
     p.wk = 1;
