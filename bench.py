@@ -350,6 +350,23 @@ def run_16k(args, torch, skg):
     return out
 
 
+def tree_verify_roofline(r16):
+    """Position of the 16K batch-8 64-node tree verify against both of its
+    rooflines: its intensity (about 251 flop per byte) sits just below the
+    ridge of 2.5 PFLOP/s dense bf16 over 8 TB/s (312), so HBM is the roof
+    that bounds it, with the matrix cores close behind.  Per-call time from
+    the budget-256 sweep's instrumented pass (events on the launch stream)."""
+    if not r16:
+        return None
+    r = r16["256"]
+    tf = r["verify_tflops"]
+    return {"kernel": "tree verify (64 nodes x GQA 4, batch 8 x 16,384 keys)", "bound": "hbm",
+            "achieved": round(r["verify_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(r["verify_gbs"] / HBM_PEAK_GBS, 4),
+            "mfma_tflops": round(tf, 1), "mfma_peak_tflops": 2500.0, "mfma_frac": round(tf / 2500.0, 4),
+            "avg_launch_ms": round(r["t_verify_ms"], 4)}
+
+
 # ------------------------------------------------------------ 4K and ragged workloads
 
 def _timed_steps(torch, step, n_steps, n_marks):
@@ -1037,6 +1054,7 @@ def main():
                      "bytes_per_launch": r1m["verify_bytes_per_launch"],
                      "avg_launch_ms": round(v_ms, 4)},
         "cpu_baseline": cpu,
+        "roofline_tree_verify_16k": tree_verify_roofline(r16),
         "ctx16k": r16,
         "ctx4k": r4k,
         "ragged": rrag,
