@@ -69,6 +69,13 @@ def accept_bytes(B, N, V):
     return B * (N + 1) * V * 4 + B * N * 4 * 2
 
 
+def _percentiles(vals):
+    """p10, p50 (median) and p90 of a list of per-call times (ms)."""
+    v = sorted(vals)
+    pick = lambda q: v[min(len(v) - 1, int(round(q * (len(v) - 1))))]  # noqa: E731
+    return [round(pick(0.1), 5), round(pick(0.5), 5), round(pick(0.9), 5)]
+
+
 # ------------------------------------------------------------ HIP graphs
 
 def graph_replay_ms(torch, fn, reps):
@@ -240,6 +247,9 @@ def run_1m(args, torch, skg):
                            ctx_draft_per_call=sum(t_ctx) / len(t_ctx),
                            fwd_draft_per_call=sum(t_fwd) / len(t_fwd)),
         call_gbs=dict(verify=v_gbs, ctx_draft=ctx_gbs, fwd_draft=fwd_gbs),
+        call_ms_percentiles={name: dict(zip(("p10", "p50", "p90"), _percentiles(vals)))
+                             for name, vals in (("verify", t_verify), ("ctx_draft", t_ctx),
+                                                ("fwd_draft", t_fwd))},
         verify_bytes_per_launch=vb, verify_avg_ms=v_avg_ms,
         graph=dict(ms_step=graph_ms, steps_per_s=1e3 / graph_ms,
                    gbs=step_bytes / (graph_ms * 1e-3) / 1e9,
@@ -1048,6 +1058,7 @@ def main():
         "graph": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r1m["graph"].items()},
         "components_ms": {k: round(v, 4) for k, v in r1m["components_ms"].items()},
         "call_gbs": {k: round(v, 1) for k, v in r1m["call_gbs"].items()},
+        "call_ms_percentiles": r1m["call_ms_percentiles"],
         "roofline": {"kernel": "verify (chain 3 over 1,048,576 keys, 8 KV heads)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
