@@ -105,7 +105,13 @@ Plan bf16_plan(const spec_dims* d, int32_t T, int64_t tiles, bool gather, bool v
   p.n_rb = (int32_t)cdiv(p.rows, p.rb);
   if (tiles < 1) tiles = 1;
   const int64_t groups = std::max<int64_t>(1, pairs * p.n_rb);
-  int64_t S = p.wk == 4 ? std::min(cdiv(kTargetWaves, groups * 4), cdiv(tiles, 4))
+  // Budget gathers aim at half as many wavefronts: each split stages its own
+  // index range and adds a partial to merge, and one workgroup per CU finishes
+  // sooner (budgets 1024 / 2048 of the 16K batch of 8: 15.0 -> 14.1 and
+  // 20.2 -> 18.8 us per call, device time; a batch-1 budget of 4096 keeps its
+  // splits).
+  const int64_t waves = gather ? kTargetWaves / 2 : kTargetWaves;
+  int64_t S = p.wk == 4 ? std::min(cdiv(waves, groups * 4), cdiv(tiles, 4))
                         : std::min(cdiv(kTargetWorkgroups, groups), tiles);
   // More splits than one merge step reads only when each split streams at
   // least 32 tiles: a second merge level costs a few microseconds, which
