@@ -203,6 +203,25 @@ def test_ragged_draft_budget(shape, budget):
     assert_close(got, ref, dt, "ragged draft budget")
 
 
+@pytest.mark.parametrize("B,Hkv,D,cap,budget", [
+    (16, 8, 64, 7000, 6100),   # 128 (sequence, KV head) pairs: the 2,048 indices one split stages set 3 splits
+    (1, 8, 128, 20000, 4090),  # one sequence: 16 splits of 8 tiles, the last one ragged
+])
+def test_budget_longer_than_one_split_stages(B, Hkv, D, cap, budget):
+    """Budget lists above the 2,048 indices a workgroup holds in LDS, with
+    repeated positions, drawn per (sequence, KV head) over ragged lengths."""
+    rng = np.random.default_rng(budget)
+    lens = rng.integers(budget, cap + 1, size=B).astype(np.int32)
+    case = synth.make_attn_case(303 + B, B=B, Hq=4 * Hkv, Hkv=Hkv, D=D, L_cap=cap, T=1,
+                                cache_len=lens, dtype="bf16", value_scale=1.0)
+    idx = np.stack([rng.integers(0, lens[b], size=(Hkv, budget)) for b in range(B)]).astype(np.int32)
+    got, lse = run_draft(case, idx=idx)
+    ref, lse_ref = oracle.draft_attn_ref(case.q, case.k, case.v, case.cache_len, scale=case.scale,
+                                         idx=idx)
+    assert_close(got, ref, "bf16", f"budget {budget} draft")
+    assert_lse_close(lse, lse_ref, 1e-3, f"budget {budget} draft lse")
+
+
 @pytest.mark.parametrize("shape", SHAPES)
 @pytest.mark.parametrize("widths", [(1,), (3,), (1, 1, 1, 1, 1), (2, 4, 6), (10, 14, 12, 8)])
 def test_ragged_verify(shape, widths):
