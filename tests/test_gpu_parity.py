@@ -272,11 +272,14 @@ def test_verify_longest_first_with_empty_splits_and_two_merge_levels():
     np.testing.assert_array_equal(pos, oracle.position_ids(case.cache_len, pad, tree.parents))
 
 
-def test_verify_batch_above_the_ordered_limit():
+@pytest.mark.parametrize("B,Hq,Hkv", [(300, 8, 2), (256, 4, 1)])
+def test_verify_batch_at_and_above_the_ordered_limit(B, Hq, Hkv):
     """A batch of 300 (above the 256 that the longest-first order ranks)
-    runs the tree verify in the plain split order."""
-    B, Hq, Hkv, D, cap = 300, 8, 2, 64, 96
-    rng = np.random.default_rng(9400)
+    runs the tree verify in the plain split order; a batch of exactly 256
+    with one KV head runs it longest first over 2 splits, with many tied
+    lengths to rank and the second split empty for contexts of up to 32."""
+    D, cap = 64, 96
+    rng = np.random.default_rng(9400 + B)
     lens = rng.integers(1, cap + 1, size=B).astype(np.int32)
     tree = synth.layered_tree(rng, (3, 4, 3))
     N = tree.n
@@ -289,5 +292,5 @@ def test_verify_batch_above_the_ordered_limit():
                                           tree.parents, scale=case.scale)
     # (unscaled values over contexts as short as one key: outputs reach about
     # 3.5, where bf16 rounding alone is |x| 2^-8, so the bar scales with them)
-    assert_close(got, ref, "bf16", "verify batch 300", magnitude=max(1.0, float(np.nanmax(np.abs(ref)))))
+    assert_close(got, ref, "bf16", f"verify batch {B}", magnitude=max(1.0, float(np.nanmax(np.abs(ref)))))
     np.testing.assert_array_equal(pos, oracle.position_ids(case.cache_len, None, tree.parents))
