@@ -96,3 +96,100 @@ def test_replays_of_a_captured_step_equal_the_eager_step():
             assert torch.equal(t, eager[n]), (rep, "eager", n)
     for w in (ws_g, ws_w, ws_v, ws_a):
         assert skg.spec_device_status(w) == 0
+
+
+def _bits(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _chain_to(parents, node):
+    path = []
+    while node >= 0:
+        path.append(int(node))
+        node = int(parents[node])
+    return path[::-1]
+
+
+@pytest.mark.parametrize("cap", [4096, 70000])
+def test_replays_of_a_captured_commit_and_compaction_equal_the_eager_calls(cap):
+    """A KV commit followed by pad compaction (above 65,536 slots with the
+    sliced pad scan), captured once.  Every replay starts from the same cache
+    and must leave exactly what the eager calls leave, which in turn is what
+    the oracle's commit and compaction give."""
+    import oracle
+    rng = np.random.default_rng(9200 + cap)
+    B, Hkv, D, depth = 2, 2, 128, 3
+    tree = synth.layered_tree(rng, (3, 4, 3))
+    N = tree.n
+    lens_np = np.array([cap - 40, cap // 3], np.int32)
+    k_np = synth.draw_normal(rng, (B, Hkv, cap, D), 1.0, "bf16")
+    v_np = synth.draw_normal(rng, (B, Hkv, cap, D), 1.0, "bf16")
+    pad_np = np.zeros((B, cap), dtype=np.uint8)
+    for b in range(B):
+        pad_np[b, :lens_np[b]] = synth.pad_groups(rng, int(lens_np[b]), n_groups=6)
+    tk_np = synth.draw_normal(rng, (B, Hkv, N, D), 1.0, "bf16")
+    tv_np = synth.draw_normal(rng, (B, Hkv, N, D), 1.0, "bf16")
+    deep = _chain_to(tree.parents, N - 1)
+    assert len(deep) == depth
+    al_np = np.array([depth, 1], np.int32)
+    ap_np = np.full((B, depth), -1, np.int32)
+    ap_np[0] = deep
+    ap_np[1, 0] = deep[0]
+
+    start = dict(k=dev(k_np), v=dev(v_np), cl=dev(lens_np), pad=dev(pad_np))
+    state = {n: t.clone() for n, t in start.items()}
+    tk, tv, al, ap = dev(tk_np), dev(tv_np), dev(al_np), dev(ap_np)
+    n_app = torch.empty(1, dtype=torch.int32, device="cuda")
+    ws_c = skg.new_workspace(skg.commit_workspace_bytes(), "cuda")
+    ws_x = skg.new_workspace(skg.compact_workspace_bytes(B), "cuda")
+
+    def reset():
+        for n, t in state.items():
+            t.copy_(start[n])
+
+    def step():
+        skg.spec_kv_commit(state["k"], state["v"], state["cl"], state["pad"], tk, tv, al, ap,
+                           n_appended=n_app, workspace=ws_c)
+        skg.spec_kv_compact(state["k"], state["v"], state["cl"], state["pad"], workspace=ws_x)
+
+    step()
+    torch.cuda.synchronize()
+    eager = {n: t.clone() for n, t in state.items()}
+    eager_n = n_app.clone()
+
+    ck, cv, ccl, cpad, P, cerr = oracle.commit_ref(k_np, v_np, lens_np, pad_np, tk_np, tv_np,
+                                                   al_np, ap_np, depth)
+    wk, wv, wcl, wpad, werr = oracle.compact_ref(ck, cv, ccl, cpad)
+    assert cerr == 0 and werr == 0
+    assert int(eager_n[0]) == P
+    np.testing.assert_array_equal(eager["cl"].cpu().numpy(), wcl)
+    np.testing.assert_array_equal(eager["pad"].cpu().numpy(), wpad)
+    gk, gv = _bits(eager["k"]), _bits(eager["v"])
+    for b in range(B):
+        n = int(wcl[b])
+        np.testing.assert_array_equal(gk[b, :, :n], wk[b, :, :n])
+        np.testing.assert_array_equal(gv[b, :, :n], wv[b, :, :n])
+
+    reset()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    reset()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(4):
+        reset()                             # eager work between the replays
+        n_app.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for n, t in state.items():
+            assert torch.equal(t, eager[n]), (rep, n)
+        assert torch.equal(n_app, eager_n), rep
+    for w in (ws_c, ws_x):
+        assert skg.spec_device_status(w) == 0
