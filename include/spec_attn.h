@@ -41,12 +41,16 @@
  *     reports and clears that word.
  *   - Workspace: a caller-allocated device buffer of at least the size the
  *     matching spec_*_workspace_bytes() returns, zero-filled before its first
- *     use.  It holds arrival counters that every call leaves at zero again,
- *     so it may be reused by any later call issued to the same stream as
- *     long as the shape arguments are the same; after a call with other
- *     shapes, zero it again (the counters sit at shape-dependent offsets).
- *     Calls that overlap in time (different streams) need separate
- *     workspaces.  Sizes depend only on the arguments, never on the device.
+ *     use.  Every workspace has the same layout: a 256-byte header (the
+ *     device error word), a 1 MiB counter region (arrival counters of the
+ *     split merges and of acceptance), then the call's own scratch (split
+ *     partials, scores).  Every call leaves the counters it used at zero
+ *     and no call's scratch overlaps the counter region, so one workspace,
+ *     zero-filled once, can be reused by any sequence of calls issued to the
+ *     same stream, of any kind and shape, as long as it is as large as each
+ *     call requires (the largest of their spec_*_workspace_bytes()).  Calls
+ *     that overlap in time (different streams) need separate workspaces.
+ *     Sizes depend only on the arguments, never on the device.
  *   - dtype SPEC_BF16 is the tuned path (bf16 inputs, fp32 accumulation, bf16
  *     outputs rounded to nearest-even); SPEC_F32 is a plain fp32 path.
  *   - head_dim must be 64 or 128.  Query head h reads KV head h / (Hq / Hkv).
@@ -76,7 +80,7 @@
 extern "C" {
 #endif
 
-#define SPEC_ABI_VERSION 1
+#define SPEC_ABI_VERSION 2
 
 typedef int32_t spec_status;
 enum {
@@ -93,6 +97,18 @@ enum { SPEC_VERIFY_FULL = 0, SPEC_VERIFY_PARTIAL = 1 };
 
 /* Element types of q, K, V and out. */
 enum { SPEC_F32 = 0, SPEC_BF16 = 1 };
+
+/* Bits of spec_dims.flags.
+ * SPEC_FLAG_DETERMINISTIC: every split of an attention call sums a fixed
+ * range of keys in a fixed order, so repeated calls with the same inputs,
+ * shapes and workspace size give bitwise equal outputs.  Without it, long
+ * single-sequence reads with few query rows (for instance a chain verify
+ * over a million cached tokens) let wavefronts take chunks of keys from a
+ * shared pool to balance the load across the chip; the sums are then the
+ * same within rounding but their order, and so the last bit of an output,
+ * can change from run to run.  Every other launch shape is deterministic
+ * either way. */
+enum { SPEC_FLAG_DETERMINISTIC = 1u };
 
 /* Bits of the device error word (spec_device_status). */
 enum {
@@ -113,6 +129,8 @@ typedef struct {
   int32_t head_dim;       /* D: 64 or 128 */
   int32_t dtype;          /* SPEC_F32 or SPEC_BF16 */
   float softmax_scale;    /* finite, > 0; scores are softmax_scale * <q, k> */
+  uint32_t flags;         /* SPEC_FLAG_* bits (0: the defaults); unknown bits are
+                             SPEC_E_INVALID */
 } spec_dims;
 
 /* A K/V pair laid out as [B][Hkv][capacity][D] with arbitrary strides (in

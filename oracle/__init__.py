@@ -35,7 +35,7 @@ values fixed by construction, hand-enumerated fixtures under
 """
 from .bf16 import decode_bf16, as_f64
 from .attention import (draft_view, draft_attn_ref, tree_depths, tree_ancestors,
-                        position_ids, verify_keys, verify_attn_ref)
+                        position_ids, verify_attn_ref)
 from .accept import argmax_ref, accept_ref, accept_bruteforce
 from .commit import commit_ref, compact_ref
 from .select import block_means_ref, block_scores_ref, select_blocks_ref
@@ -43,7 +43,7 @@ from .partial import gather_ref, verify_mode_ref
 from .ring import ring_draft_ref, ring_from_logical, ring_slot
 
 __all__ = ["decode_bf16", "as_f64", "draft_view", "draft_attn_ref", "tree_depths",
-           "tree_ancestors", "position_ids", "verify_keys", "verify_attn_ref",
+           "tree_ancestors", "position_ids", "verify_attn_ref",
            "argmax_ref", "accept_ref", "accept_bruteforce", "commit_ref",
            "block_means_ref", "block_scores_ref", "select_blocks_ref", "gather_ref",
            "verify_mode_ref", "ring_draft_ref", "ring_from_logical", "ring_slot"]

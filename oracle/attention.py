@@ -152,16 +152,6 @@ def position_ids(cache_len, pad, parents) -> np.ndarray:
     return np.stack(out).astype(np.int64)
 
 
-def verify_keys(L_b: int, pad_b, parents_b, i: int):
-    """(cache slots, tree nodes) visible to tree node i: every cache slot
-    j < L_b that is not padding, then node i and its ancestors in node order."""
-    slots = np.arange(L_b)
-    if pad_b is not None:
-        slots = slots[np.asarray(pad_b[:L_b]) == 0]
-    nodes = np.nonzero(tree_ancestors(parents_b)[i])[0]
-    return slots, nodes
-
-
 def verify_attn_ref(q, k, v, cache_len, tree_k, tree_v, parents, *, scale: float,
                     pad=None, pairs=None, rows=None):
     """Tree-masked verify attention (SpecMemo review, "What carries the

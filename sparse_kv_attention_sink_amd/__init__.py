@@ -7,7 +7,7 @@ that ABI.  Build the library with ``python -m sparse_kv_attention_sink_amd.build
 from ._lib import (  # noqa: F401
     EXPORTED, LIB_PATH, SPEC_BF16, SPEC_DEV_CACHE_LEN, SPEC_DEV_COMMIT, SPEC_DEV_DEPTH,
     SPEC_DEV_INDEX, SPEC_DEV_PARENT, SPEC_E_DEVICE_RANGE, SPEC_E_HIP, SPEC_E_INVALID,
-    SPEC_E_UNSUPPORTED, SPEC_E_WORKSPACE, SPEC_F32, SPEC_OK, SpecDims, SpecError, SpecKV,
+    SPEC_E_UNSUPPORTED, SPEC_E_WORKSPACE, SPEC_F32, SPEC_FLAG_DETERMINISTIC, SPEC_OK, SpecDims, SpecError, SpecKV,
     accept_workspace_bytes, commit_workspace_bytes, compact_workspace_bytes, draft_workspace_bytes,
     load, make_dims,
     new_workspace, spec_accept_greedy, spec_attn_draft_ring, spec_attn_draft_sparse,

@@ -25,6 +25,7 @@ SPEC_E_HIP = -4
 SPEC_E_DEVICE_RANGE = -5
 SPEC_F32 = 0
 SPEC_BF16 = 1
+SPEC_FLAG_DETERMINISTIC = 1
 SPEC_DEV_CACHE_LEN = 1
 SPEC_DEV_INDEX = 2
 SPEC_DEV_PARENT = 4
@@ -46,7 +47,8 @@ EXPORTED = [
 class SpecDims(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
                 ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-                ("dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float)]
+                ("dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+                ("flags", ctypes.c_uint32)]
 
 
 class SpecKV(ctypes.Structure):
@@ -148,8 +150,9 @@ def _on_gpu(*ts):
             raise ValueError("all tensors must be on the GPU")
 
 
-def make_dims(B, Hq, Hkv, D, dtype_code, scale=None) -> SpecDims:
-    return SpecDims(B, Hq, Hkv, D, dtype_code, 1.0 / math.sqrt(D) if scale is None else scale)
+def make_dims(B, Hq, Hkv, D, dtype_code, scale=None, deterministic=False) -> SpecDims:
+    return SpecDims(B, Hq, Hkv, D, dtype_code, 1.0 / math.sqrt(D) if scale is None else scale,
+                    SPEC_FLAG_DETERMINISTIC if deterministic else 0)
 
 
 def _kv(k: torch.Tensor, v: torch.Tensor) -> SpecKV:
@@ -178,9 +181,11 @@ def new_workspace(nbytes: int, device) -> torch.Tensor:
 
 
 def spec_attn_draft_sparse(q, k_cache, v_cache, cache_len, *, n_sink=0, window=0, idx=None,
-                           scale=None, out=None, lse=None, workspace=None, want_lse=True):
+                           scale=None, out=None, lse=None, workspace=None, want_lse=True,
+                           deterministic=False):
     """Draft attention over sink + window (idx None) or a budget list idx
-    ``[B, 1 or Hkv, budget]`` int32.  Returns (out, lse)."""
+    ``[B, 1 or Hkv, budget]`` int32.  ``deterministic`` sets
+    SPEC_FLAG_DETERMINISTIC.  Returns (out, lse)."""
     lib = load()
     _on_gpu(q, k_cache, v_cache, cache_len, idx)
     if q.dim() != 4 or not q.is_contiguous():
@@ -191,7 +196,7 @@ def spec_attn_draft_sparse(q, k_cache, v_cache, cache_len, *, n_sink=0, window=0
     if cache_len.dtype != torch.int32 or cache_len.numel() != B or not cache_len.is_contiguous():
         raise ValueError("cache_len must be a contiguous int32 [B] tensor")
     kv = _kv(k_cache, v_cache)
-    dims = make_dims(B, Hq, k_cache.shape[1], D, _dtype_code(q), scale)
+    dims = make_dims(B, Hq, k_cache.shape[1], D, _dtype_code(q), scale, deterministic)
     budget, isb, ish = 0, 0, 0
     if idx is not None:
         if idx.dtype != torch.int32 or idx.dim() != 3 or idx.shape[0] != B or idx.stride(2) != 1:
@@ -218,7 +223,7 @@ def spec_attn_draft_sparse(q, k_cache, v_cache, cache_len, *, n_sink=0, window=0
 
 
 def spec_attn_draft_ring(q, k_ring, v_ring, cache_len, *, n_sink, window, ring, scale=None,
-                         out=None, lse=None, workspace=None, want_lse=True):
+                         out=None, lse=None, workspace=None, want_lse=True, deterministic=False):
     """Window draft over a ring cache ``[B, Hkv, >= n_sink + ring, D]``
     (position p >= n_sink at slot n_sink + (p - n_sink) % ring); ``cache_len``
     holds the logical lengths.  Returns (out, lse)."""
@@ -232,7 +237,7 @@ def spec_attn_draft_ring(q, k_ring, v_ring, cache_len, *, n_sink, window, ring, 
     if cache_len.dtype != torch.int32 or cache_len.numel() != B or not cache_len.is_contiguous():
         raise ValueError("cache_len must be a contiguous int32 [B] tensor")
     kv = _kv(k_ring, v_ring)
-    dims = make_dims(B, Hq, k_ring.shape[1], D, _dtype_code(q), scale)
+    dims = make_dims(B, Hq, k_ring.shape[1], D, _dtype_code(q), scale, deterministic)
     if out is None:
         out = torch.empty_like(q)
     if lse is None and want_lse:
@@ -249,10 +254,11 @@ def spec_attn_draft_ring(q, k_ring, v_ring, cache_len, *, n_sink, window, ring, 
 
 def spec_attn_verify_tree(q, k_cache, v_cache, cache_len, tree_k, tree_v, parents, *, pad=None,
                           scale=None, out=None, lse=None, pos_ids=None, want_lse=True,
-                          want_pos_ids=True, workspace=None):
+                          want_pos_ids=True, workspace=None, deterministic=False):
     """Tree-masked verify attention.  q ``[B, N, Hq, D]``; tree K/V
     ``[B, Hkv, N, D]``; parents int32 ``[N]`` or ``[B, N]``; pad uint8
-    ``[B, >= L_cap]`` or None.  Returns (out, lse, pos_ids)."""
+    ``[B, >= L_cap]`` or None; ``deterministic`` sets
+    SPEC_FLAG_DETERMINISTIC.  Returns (out, lse, pos_ids)."""
     lib = load()
     _on_gpu(q, k_cache, v_cache, cache_len, tree_k, tree_v, parents, pad)
     if q.dim() != 4 or not q.is_contiguous():
@@ -271,7 +277,7 @@ def spec_attn_verify_tree(q, k_cache, v_cache, cache_len, tree_k, tree_v, parent
         raise ValueError("parents must be [N] or [B, N]")
     kv = _kv(k_cache, v_cache)
     tkv = _kv(tree_k, tree_v)
-    dims = make_dims(B, Hq, k_cache.shape[1], D, _dtype_code(q), scale)
+    dims = make_dims(B, Hq, k_cache.shape[1], D, _dtype_code(q), scale, deterministic)
     pad_sb = 0
     if pad is not None:
         if pad.dtype != torch.uint8 or pad.dim() != 2 or pad.shape[0] != B or pad.stride(1) != 1:

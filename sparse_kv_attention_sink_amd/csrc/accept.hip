@@ -196,7 +196,7 @@ __global__ __launch_bounds__(256) void accept_kernel(
               bonus, err);
 }
 
-size_t accept_part_offset(int B) { return kHeaderBytes + align_up((size_t)B * 4, 256); }
+size_t accept_part_offset(int) { return kScratchOff; }
 
 hipError_t launch_accept(int B, int N, int V, const float* logits, const int32_t* tokens,
                          const int32_t* parents, int64_t parents_sb, int max_depth,

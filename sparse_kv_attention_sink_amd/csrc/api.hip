@@ -52,6 +52,8 @@ spec_status check_dims(const spec_dims* d) {
     return fail(SPEC_E_UNSUPPORTED, "dtype %d (supported: SPEC_F32, SPEC_BF16)", d->dtype);
   if (!(d->softmax_scale > 0.f) || !isfinite(d->softmax_scale))
     return fail(SPEC_E_INVALID, "softmax_scale must be finite and > 0");
+  if (d->flags & ~(uint32_t)SPEC_FLAG_DETERMINISTIC)
+    return fail(SPEC_E_INVALID, "unknown flag bits 0x%x", d->flags & ~(uint32_t)SPEC_FLAG_DETERMINISTIC);
   return SPEC_OK;
 }
 
@@ -138,16 +140,29 @@ Plan bf16_plan(const spec_dims* d, int32_t T, int64_t tiles, bool gather, bool v
     p.total = 0;
     return p;
   }
+  // The counters (two per sequence, n_blk + 2 per (pair, row block)) must
+  // fit the workspace's fixed counter region; a second merge level is
+  // given up before the shape is refused.
+  const auto counter_words = [&](int64_t splits) {
+    return 2 * (int64_t)std::max(0, d->batch) + groups * (cdiv(splits, kMergeFan) + 2);
+  };
+  if (counter_words(S) > (int64_t)kCounterWords) S = std::min<int64_t>(S, kMergeFan);
+  if (S < lo || counter_words(S) > (int64_t)kCounterWords) {
+    p.total = 0;
+    return p;
+  }
   p.tps = (int32_t)cdiv(tiles, S);
   p.splits = (int32_t)cdiv(tiles, p.tps);
   p.n_blk = (int32_t)cdiv(p.splits, kMergeFan);
   // Long register-staged splits take their tiles in chunks (dynamic
   // balancing across XCDs); budget gathers keep fixed ranges (their indices
-  // are staged per range).
-  if (p.wk == 4 && !gather && p.splits > 1 && tiles >= (int64_t)p.splits * 32) p.dyn = kChunkTiles;
-  size_t off = kHeaderBytes;
-  p.cnt_off = off;
-  off = align_up(off + (size_t)(groups * (p.n_blk + 2) + 2 * std::max(0, d->batch)) * sizeof(uint32_t), 256);
+  // are staged per range), and so does the deterministic mode (which wave
+  // sums which tiles would otherwise depend on timing).
+  if (p.wk == 4 && !gather && p.splits > 1 && tiles >= (int64_t)p.splits * 32 &&
+      !(d->flags & SPEC_FLAG_DETERMINISTIC))
+    p.dyn = kChunkTiles;
+  p.cnt_off = kHeaderBytes;
+  size_t off = kScratchOff;
   if (p.splits > 1) {
     const size_t n = (size_t)groups * p.splits * p.rb;
     p.o_off = off;
@@ -185,7 +200,7 @@ Plan f32_plan(const spec_dims* d, int32_t T, int64_t keys, bool verify) {
   p.rb = 1;
   p.n_rb = p.rows;
   f32_splits(p, pairs, keys);
-  size_t off = kHeaderBytes;
+  size_t off = kScratchOff;
   if (p.splits > 1) {
     const size_t n = (size_t)pairs * p.n_rb * p.splits;
     p.o_off = off;
@@ -226,15 +241,16 @@ int accept_vsplits(int64_t rows, int64_t V) {
   return (int)vs;
 }
 
-// header | fp32 block scores [B][Hkv][max_blocks]
+// header | counter region (unused) | fp32 block scores [B][Hkv][max_blocks]
 size_t select_bytes(const spec_dims* d, int32_t max_blocks) {
-  return kHeaderBytes +
+  return kScratchOff +
          align_up((size_t)std::max(d->batch, 0) * d->n_kv_heads * std::max(max_blocks, 0) * sizeof(float), 256);
 }
 
-// header | per-sequence arrival counters | (value, index) winner per slice
-size_t accept_bytes(int64_t batch, int64_t rows, int vs) {
-  return align_up(kHeaderBytes + align_up((size_t)batch * 4, 256) + (size_t)rows * vs * 8, 256);
+// header | counter region (one arrival counter per sequence first) |
+// (value, index) winner per slice
+size_t accept_bytes(int64_t, int64_t rows, int vs) {
+  return align_up(kScratchOff + (size_t)rows * vs * 8, 256);
 }
 
 int64_t draft_max_view(const spec_kv* cache, int32_t Tq, int32_t n_sink, int32_t window,
@@ -540,6 +556,9 @@ spec_status spec_accept_greedy(int32_t batch, int32_t n_nodes, int32_t vocab, co
     return fail(SPEC_E_INVALID, "int32 arrays must be 4-byte aligned");
   if (parents_stride_b != 0 && parents_stride_b < n_nodes)
     return fail(SPEC_E_INVALID, "parents_stride_b must be 0 (shared) or >= n_nodes");
+  if ((size_t)batch > kCounterWords)
+    return fail(SPEC_E_UNSUPPORTED, "batch %d exceeds the %zu arrival counters of the workspace", batch,
+                kCounterWords);
   const int64_t rows = (int64_t)batch * (n_nodes + 1);
   const int vs = accept_vsplits(rows, vocab);
   const size_t need = accept_bytes(batch, rows, vs);
@@ -615,9 +634,10 @@ spec_status spec_kv_commit(int32_t batch, int32_t n_kv_heads, int32_t head_dim, 
 
 size_t spec_commit_workspace_bytes(void) { return kHeaderBytes; }
 
-// header | [B][kCompactSlices][2] int32: first pad slot and pad count per slice of the pad bytes
+// header | counter region (unused) | [B][kCompactSlices][2] int32: first pad
+// slot and pad count per slice of the pad bytes
 size_t spec_compact_workspace_bytes(int32_t batch) {
-  return kHeaderBytes + align_up((size_t)std::max(batch, 0) * kCompactSlices * 2 * sizeof(int32_t), 256);
+  return kScratchOff + align_up((size_t)std::max(batch, 0) * kCompactSlices * 2 * sizeof(int32_t), 256);
 }
 
 spec_status spec_kv_compact(int32_t batch, int32_t n_kv_heads, int32_t head_dim, int32_t dtype,
@@ -656,7 +676,7 @@ spec_status spec_kv_compact(int32_t batch, int32_t n_kv_heads, int32_t head_dim,
   a.cache_len = cache_len;
   a.pad = pad;
   a.pad_sb = pad_stride_b;
-  a.summary = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) + kHeaderBytes);
+  a.summary = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) + kScratchOff);
   a.sliced = cache->capacity > kCompactScanSlots ? 1 : 0;
   a.err = static_cast<uint32_t*>(workspace);
   hipError_t e = launch_kv_compact(a, static_cast<hipStream_t>(stream));
@@ -773,7 +793,7 @@ spec_status spec_select_blocks(const spec_dims* dims, const void* q, int32_t n_q
   a.pad_sb = pad_stride_b;
   a.idx = idx;
   a.scores = scores_or_null;
-  a.sc_ws = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + kHeaderBytes);
+  a.sc_ws = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + kScratchOff);
   a.err = static_cast<uint32_t*>(workspace);
   hipError_t e = launch_select_blocks(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "block selection launch");

@@ -21,6 +21,15 @@
 namespace spec {
 
 constexpr size_t kHeaderBytes = 256;           // [0,4): device error word
+// Workspace layout shared by every call: the header, then a counter region
+// of fixed size (arrival counters, chunk pools; every call leaves the words
+// it uses at zero), then the call's own scratch (split partials, scores,
+// slice summaries).  Because no call's scratch ever overlaps any call's
+// counters, one zero-filled workspace serves any sequence of calls on a
+// stream, whatever their shapes and kinds.
+constexpr size_t kCounterBytes = size_t(1) << 20;
+constexpr size_t kCounterWords = kCounterBytes / 4;
+constexpr size_t kScratchOff = kHeaderBytes + kCounterBytes;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr int kMaxNodes = 64;                  // one uint64 ancestor mask per node

@@ -16,3 +16,18 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def golden_dir():
     return os.path.join(ROOT, "tests", "golden")
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    """Observed parity errors: max abs error and the fraction of the
+    per-element bar each comparison used (the largest first)."""
+    try:
+        from helpers import ERROR_LOG
+    except ImportError:
+        return
+    if not ERROR_LOG:
+        return
+    tr = terminalreporter
+    tr.section("parity errors (max |err|, share of the per-element bar)")
+    for what, dtype, err, used in sorted(ERROR_LOG, key=lambda r: -r[3]):
+        tr.write_line(f"{used:6.3f}  {err:.3e}  {dtype:4s}  {what}")

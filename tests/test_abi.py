@@ -47,12 +47,39 @@ def test_every_declared_function_is_exported(lib):
 
 
 def test_abi_version(lib):
-    assert lib.spec_abi_version() == 1
+    assert lib.spec_abi_version() == 2
     assert lib.spec_status_string(skg.SPEC_E_WORKSPACE) == b"SPEC_E_WORKSPACE"
 
 
-def dims(B=1, Hq=32, Hkv=8, D=128, dtype=skg.SPEC_BF16, scale=0.088):
-    return SpecDims(B, Hq, Hkv, D, dtype, scale)
+def dims(B=1, Hq=32, Hkv=8, D=128, dtype=skg.SPEC_BF16, scale=0.088, flags=0):
+    return SpecDims(B, Hq, Hkv, D, dtype, scale, flags)
+
+
+# Every workspace: a 256-byte header, the 1 MiB counter region, then scratch.
+SCRATCH = 256 + (1 << 20)
+
+
+def test_every_scratch_region_starts_after_the_counter_region(lib):
+    """No call's scratch may overlap the counter region, whatever its shape,
+    so that one workspace serves calls of every kind and shape."""
+    for B in (1, 8, 16, 300):
+        d = dims(B=B)
+        for T, view in ((1, 256), (3, 4100), (1, 1 << 19), (8, 64)):
+            assert skg.draft_workspace_bytes(d, T, view) >= SCRATCH
+        for N, cap in ((3, 1 << 20), (64, 16384), (44, 32768), (5, 4096)):
+            assert skg.verify_workspace_bytes(d, N, cap) >= SCRATCH
+        assert skg.accept_workspace_bytes(B, 64, 128256) >= SCRATCH + B * 65 * 8
+        assert lib.spec_compact_workspace_bytes(B) >= SCRATCH
+        assert lib.spec_select_workspace_bytes(ctypes.byref(d), 16) >= SCRATCH
+        dd = dims(B=B, dtype=skg.SPEC_F32, D=64, Hq=2, Hkv=1)
+        assert skg.verify_workspace_bytes(dd, 15, 512) >= SCRATCH
+        assert skg.draft_workspace_bytes(dd, 1, 68) >= SCRATCH
+
+
+def test_unknown_flag_bits_are_rejected(lib):
+    assert skg.draft_workspace_bytes(dims(flags=skg.SPEC_FLAG_DETERMINISTIC), 1, 256) > 0
+    assert skg.draft_workspace_bytes(dims(flags=2), 1, 256) == 0
+    assert b"flag" in lib.spec_last_error()
 
 
 def test_workspace_sizes_are_device_free_and_monotone(lib):
@@ -320,8 +347,8 @@ def test_empty_batch_is_a_no_op(lib):
     assert select_call(lib, dims(B=0)) == skg.SPEC_OK
     assert gather_call(lib, B=0) == skg.SPEC_OK
     d = dims(B=8)
-    assert lib.spec_select_workspace_bytes(ctypes.byref(d), 0) == 256
-    assert lib.spec_select_workspace_bytes(ctypes.byref(d), 1024) == 256 + 8 * 8 * 1024 * 4
+    assert lib.spec_select_workspace_bytes(ctypes.byref(d), 0) == SCRATCH
+    assert lib.spec_select_workspace_bytes(ctypes.byref(d), 1024) == SCRATCH + 8 * 8 * 1024 * 4
 
 
 def test_binding_fails_loudly_without_library(tmp_path):

@@ -49,9 +49,14 @@ def verify_pair_ref(d, b, g, cache_len_b, parents, pad=None):
 
 # ------------------------------------------------------------ 1M layer
 
-@pytest.fixture(scope="module")
-def layer1m():
-    d = dg.layer_1m(0)
+# Two seeded layers of the 32: layer 0 and layer 17 (seeds 4000 and 4017).
+LAYERS_CHECKED = (0, 17)
+
+
+@pytest.fixture(scope="module", params=LAYERS_CHECKED, ids=[f"layer{l}" for l in LAYERS_CHECKED])
+def layer1m(request):
+    d = dg.layer_1m(request.param)
+    d["layer"] = request.param
     torch.cuda.synchronize()
     yield d
     del d
@@ -61,24 +66,38 @@ def layer1m():
 L1M = 1 << 20
 
 
-def test_1m_verify_chain3_sampled(layer1m):
+@pytest.mark.parametrize("deterministic", [False, True], ids=["pool", "deterministic"])
+def test_1m_verify_chain3_sampled(layer1m, deterministic):
+    """The chain-3 verify over the whole layer, three calls in a row on one
+    workspace (the pool's counters must start over every call), each within
+    the bar on two KV heads; the deterministic mode's three outputs are
+    bitwise equal."""
     d = layer1m
     dims = skg.make_dims(1, 32, 8, 128, skg.SPEC_BF16)
     ws = skg.new_workspace(skg.verify_workspace_bytes(dims, 3, L1M), "cuda")
     cl = torch.tensor([L1M], dtype=torch.int32, device="cuda")
     par = torch.tensor([-1, 0, 1], dtype=torch.int32, device="cuda")
-    out, lse, pos = skg.spec_attn_verify_tree(d["verify_q"], d["k"], d["v"], cl, d["tree_k"],
-                                              d["tree_v"], par, workspace=ws)
-    torch.cuda.synchronize()
-    assert skg.spec_device_status(ws) == 0
-    got = host64(out)
-    lse = lse.cpu().numpy().astype(np.float64)
-    assert np.all(np.isfinite(got))
-    np.testing.assert_array_equal(pos.cpu().numpy(), [[L1M, L1M + 1, L1M + 2]])
-    for g in (0, 5):
-        ref, lse_ref = verify_pair_ref(d, 0, g, L1M, np.array([-1, 0, 1]))
-        assert_close(got[:, :, g * G:(g + 1) * G], ref, "bf16", f"1M verify kv head {g}")
-        assert_lse_close(lse[:, :, g * G:(g + 1) * G], lse_ref, 1e-3, "1M verify lse")
+    refs = {g: verify_pair_ref(d, 0, g, L1M, np.array([-1, 0, 1])) for g in (0, 5)}
+    runs = []
+    for rep in range(3):
+        out, lse, pos = skg.spec_attn_verify_tree(d["verify_q"], d["k"], d["v"], cl, d["tree_k"],
+                                                  d["tree_v"], par, workspace=ws,
+                                                  deterministic=deterministic)
+        torch.cuda.synchronize()
+        assert skg.spec_device_status(ws) == 0
+        got = host64(out)
+        lse = lse.cpu().numpy().astype(np.float64)
+        assert np.all(np.isfinite(got))
+        np.testing.assert_array_equal(pos.cpu().numpy(), [[L1M, L1M + 1, L1M + 2]])
+        for g, (ref, lse_ref) in refs.items():
+            assert_close(got[:, :, g * G:(g + 1) * G], ref, "bf16",
+                         f"1M layer {d['layer']} verify kv head {g} call {rep}"
+                         + (" (deterministic)" if deterministic else ""))
+            assert_lse_close(lse[:, :, g * G:(g + 1) * G], lse_ref, 1e-3, "1M verify lse")
+        runs.append((bits(out), lse))
+    if deterministic:
+        for o, l in runs[1:]:
+            assert np.array_equal(o, runs[0][0]) and np.array_equal(l, runs[0][1])
 
 
 @pytest.mark.parametrize("which", ["ctx", "fwd"])
@@ -105,7 +124,8 @@ def test_1m_window_draft_sampled(layer1m, which):
         qq = bits(q[:, :, g * G:(g + 1) * G])
         ref, lse_ref = oracle.draft_attn_ref(qq, kk, vv, np.array([len(keep)]),
                                              scale=1 / math.sqrt(128), n_sink=4, window=4096)
-        assert_close(got[:, :, g * G:(g + 1) * G], ref, "bf16", f"1M {which} draft head {g}")
+        assert_close(got[:, :, g * G:(g + 1) * G], ref, "bf16",
+                     f"1M layer {d['layer']} {which} draft head {g}")
         assert_lse_close(lse[:, :, g * G:(g + 1) * G], lse_ref, 1e-3, "1M draft lse")
 
 
@@ -173,5 +193,4 @@ def test_ragged_verify_peaked_sampled():
         ref, _ = verify_pair_ref(d, b, g, int(d["lens"][b]), d["tree"].parents, d["pad"])
         mag = np.abs(ref[~np.isnan(ref)]).max()
         assert mag > 0.5
-        assert_close(got[b:b + 1, :, g * G:(g + 1) * G], ref, "bf16", f"peaked pair ({b}, {g})",
-                     magnitude=mag)
+        assert_close(got[b:b + 1, :, g * G:(g + 1) * G], ref, "bf16", f"peaked pair ({b}, {g})")
