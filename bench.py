@@ -218,6 +218,43 @@ def run_1m(args, torch, skg):
     del graph
     for w in (ws_v, ws_c, ws_f, ws_a):
         assert skg.spec_device_status(w) == 0, "device range error in the graph replays"
+    assert graph_ints_equal, "graph replay changed an integer output"
+    assert graph_att_diff <= 1e-2, f"graph replay moved an attention output by {graph_att_diff}"
+
+    # The verify in both modes, back to back over every layer: the pooled
+    # default and SPEC_FLAG_DETERMINISTIC (fixed split ranges), whose outputs
+    # must repeat bit for bit.
+    def verify_pass(det):
+        for lay in layers:
+            skg.spec_attn_verify_tree(lay["verify_q"], lay["k"], lay["v"], cache_len,
+                                      lay["tree_k"], lay["tree_v"], parents, out=v_out, lse=v_lse,
+                                      pos_ids=v_pos, workspace=ws_v, deterministic=det)
+    mode_ms = {}
+    n_layers = len(layers)
+    for det in (False, True, False, True):
+        verify_pass(det)
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record()
+        for _ in range(max(args.steps // 2, 2)):
+            verify_pass(det)
+        b.record()
+        torch.cuda.synchronize()
+        mode_ms.setdefault(det, []).append(a.elapsed_time(b) / (max(args.steps // 2, 2) * n_layers))
+    det_bits = []
+    for _ in range(3):
+        skg.spec_attn_verify_tree(layers[0]["verify_q"], layers[0]["k"], layers[0]["v"], cache_len,
+                                  layers[0]["tree_k"], layers[0]["tree_v"], parents, out=v_out,
+                                  lse=v_lse, pos_ids=v_pos, workspace=ws_v, deterministic=True)
+        det_bits.append((v_out.view(torch.int16).clone(), v_lse.clone()))
+    torch.cuda.synchronize()
+    det_equal = all(torch.equal(x[0], det_bits[0][0]) and torch.equal(x[1], det_bits[0][1])
+                    for x in det_bits[1:])
+    assert det_equal, "deterministic verify differs between runs"
+    verify_modes = {"pooled_ms": round(min(mode_ms[False]), 4),
+                    "deterministic_ms": round(min(mode_ms[True]), 4),
+                    "deterministic_cost": round(min(mode_ms[True]) / min(mode_ms[False]) - 1, 4),
+                    "deterministic_runs_bitwise_equal": det_equal}
 
     t_verify = [m[0].elapsed_time(m[1]) for st in marks for m in st]
     t_ctx = [m[1].elapsed_time(m[2]) for st in marks for m in st]
@@ -255,6 +292,7 @@ def run_1m(args, torch, skg):
                    gbs=step_bytes / (graph_ms * 1e-3) / 1e9,
                    replay_int_outputs_equal=graph_ints_equal,
                    replay_attn_max_abs_diff=graph_att_diff),
+        verify_modes=verify_modes,
     )
     return res, layers
 
@@ -264,25 +302,27 @@ def synth_seed(c):
     return synth.SEEDS[c]
 
 
-# ------------------------------------------------------------ 16K workload
+# ------------------------------------------------------------ 8K and 16K workloads
 
-def run_16k(args, torch, skg):
-    """Batch 8 x 16K context; per draft budget B: t_verify(64-node tree) +
-    4 t_draft(B) + t_accept.  The KV is rotated over 16 copies (8 GiB) so
-    the 256 MB Infinity Cache does not serve the timed reads."""
+def run_ctx(args, torch, skg, L, seed):
+    """Batch 8 x L context (16,384, or the 8,192 point of BudgetDraft's
+    4K / 8K / 16K sweep); per draft budget B: t_verify(64-node tree) +
+    4 t_draft(B) + t_accept.  The KV is rotated over 16 copies (8 GiB at
+    16K, 4 GiB at 8K) so the 256 MB Infinity Cache does not serve the timed
+    reads."""
     import numpy as np
     import synth
     dev = torch.device("cuda:0")
-    Bsz, L, ROT = 8, 16384, 16
+    Bsz, ROT = 8, 16
     s = 1.0 / math.sqrt(D)
     gen = torch.Generator(device=dev)
-    gen.manual_seed(synth.SEEDS[3] + 500)
+    gen.manual_seed(seed + 500)
     kvs = []
     for _ in range(ROT):
         k = (torch.randn((Bsz, HKV, L, D), generator=gen, device=dev) * s).to(torch.bfloat16)
         v = (torch.randn((Bsz, HKV, L, D), generator=gen, device=dev) * s).to(torch.bfloat16)
         kvs.append((k, v))
-    tree = synth.layered_tree(np.random.default_rng(synth.SEEDS[3]), (10, 18, 18, 18))
+    tree = synth.layered_tree(np.random.default_rng(seed), (10, 18, 18, 18))
     N = tree.n
     parents = torch.from_numpy(tree.parents).to(dev)
     vq = (torch.randn((Bsz, N, HQ, D), generator=gen, device=dev) * s).to(torch.bfloat16)
@@ -292,7 +332,7 @@ def run_16k(args, torch, skg):
     cache_len = torch.full((Bsz,), L, dtype=torch.int32, device=dev)
     logits = torch.randn((Bsz, N + 1, VOCAB), generator=gen, device=dev)
     tokens = torch.randint(0, VOCAB, (Bsz, N), generator=gen, device=dev, dtype=torch.int32)
-    rng = np.random.default_rng(synth.SEEDS[3] + 1)
+    rng = np.random.default_rng(seed + 1)
     dims = skg.make_dims(Bsz, HQ, HKV, D, skg.SPEC_BF16)
     ws_v = skg.new_workspace(skg.verify_workspace_bytes(dims, N, L), dev)
     ws_a = skg.new_workspace(skg.accept_workspace_bytes(Bsz, N, VOCAB), dev)
@@ -358,6 +398,81 @@ def run_16k(args, torch, skg):
     del kvs
     torch.cuda.empty_cache()
     return out
+
+
+def run_16k(args, torch, skg):
+    import synth
+    return run_ctx(args, torch, skg, 16384, synth.SEEDS[3])
+
+
+def run_8k(args, torch, skg):
+    import synth
+    return run_ctx(args, torch, skg, 8192, synth.SEEDS["8k"])
+
+
+# ------------------------------------------------------------ machine probes
+
+def run_probes(torch):
+    """What this GPU delivers, measured with the probe kernels: the HBM read
+    rate of a plain streaming read of 4 GiB through each load path of the
+    attention kernels (best over a few launch shapes), and the floor of a
+    short call: an empty launch and a one-pass read of a draft call's 16.8 MB
+    (the 1M window draft's K/V), both as HIP-graph replays of back-to-back
+    launches, the reads rotating over 32 buffers (537 MB) so the Infinity
+    Cache does not serve them."""
+    import sparse_kv_attention_sink_amd._probe as pr
+    pr.load()
+    dev = torch.device("cuda:0")
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device=dev)
+    nbytes = 4 << 30
+    buf = torch.ones(nbytes // 2, dtype=torch.bfloat16, device=dev)
+
+    def timed(fn, reps=6):
+        fn()
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    shapes = {}
+    for wg in (1024, 2048, 4096, 8192):
+        for inf in (4, 8, 16):
+            ms = timed(lambda: pr.read(buf, wg, inf, sink))
+            shapes[f"regs_wg{wg}_inflight{inf}"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    for wg in (256, 512):
+        for st in (4, 6, 8):
+            if wg == 512 and st > 4:
+                continue   # two workgroups of more than 4 stages exceed the LDS of a CU
+            ms = timed(lambda: pr.read_lds(buf, wg, st, sink))
+            shapes[f"lds_wg{wg}_stages{st}"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    del buf
+    best_regs = max(v for k, v in shapes.items() if k.startswith("regs"))
+    best_lds = max(v for k, v in shapes.items() if k.startswith("lds"))
+
+    g_ms, graph = graph_replay_ms(torch, lambda: [pr.empty(1, sink) for _ in range(100)], 10)
+    del graph
+    empty1 = g_ms / 100 * 1e3
+    g_ms, graph = graph_replay_ms(torch, lambda: [pr.empty(256, sink) for _ in range(100)], 10)
+    del graph
+    empty256 = g_ms / 100 * 1e3
+    small = 4100 * 4096   # the 1M window draft's K and V over 8 KV heads: 16,793,600 bytes
+    bufs = [torch.ones(small // 2, dtype=torch.bfloat16, device=dev) for _ in range(32)]
+    reads = {}
+    for wg in (256, 512, 1024):
+        g_ms, graph = graph_replay_ms(torch, lambda: [pr.read(b, wg, 4, sink) for b in bufs], 4)
+        del graph
+        reads[f"wg{wg}"] = round(g_ms / len(bufs) * 1e3, 2)
+    del bufs
+    torch.cuda.empty_cache()
+    return {"stream_read_gbs": max(best_regs, best_lds), "stream_read_regs_gbs": best_regs,
+            "stream_read_lds_gbs": best_lds, "stream_read_bytes": nbytes, "shapes": shapes,
+            "empty_launch_us": {"1_workgroup": round(empty1, 2), "256_workgroups": round(empty256, 2)},
+            "read_16_8mb_us": reads, "read_16_8mb_floor_us": min(reads.values())}
 
 
 def tree_verify_roofline(r16):
@@ -995,8 +1110,13 @@ def main():
         return
 
     if args.skip_1m:
-        print(json.dumps({"ctx16k": run_16k(args, torch, skg)}), flush=True)
+        print(json.dumps({"ctx16k": run_16k(args, torch, skg),
+                          "ctx8k": run_8k(args, torch, skg)}), flush=True)
         return
+    probes = run_probes(torch)
+    log(f"[bench] stream read {probes['stream_read_gbs']} GB/s (registers "
+        f"{probes['stream_read_regs_gbs']}, LDS copies {probes['stream_read_lds_gbs']}); empty "
+        f"launch {probes['empty_launch_us']} us; 16.8 MB read {probes['read_16_8mb_floor_us']} us")
     r1m, layers = run_1m(args, torch, skg)
     log(f"[bench] 1M step: {r1m['ms_step']:.3f} ms, {r1m['gbs']:.1f} GB/s")
     cpu = None
@@ -1013,6 +1133,7 @@ def main():
     del layers
     torch.cuda.empty_cache()
     r16 = None if args.skip_16k else run_16k(args, torch, skg)
+    r8k = None if args.skip_16k else run_8k(args, torch, skg)
     r4k = run_4k(args, torch, skg)
     log(f"[bench] 4K step: {r4k['ms_step']} ms ({r4k['steps_per_s']} steps/s)")
     rrag = run_ragged(args, torch, skg)
@@ -1034,6 +1155,24 @@ def main():
 
     v_ms = r1m["verify_avg_ms"]
     achieved = r1m["verify_bytes_per_launch"] / (v_ms * 1e-3) / 1e9
+    ceil = probes["stream_read_gbs"]
+    # every kernel's rate as a fraction of the measured stream-read ceiling
+    vs_stream = {"verify_1m": round(achieved / ceil, 4),
+                 "ctx_draft_1m": round(r1m["call_gbs"]["ctx_draft"] / ceil, 4),
+                 "fwd_draft_1m": round(r1m["call_gbs"]["fwd_draft"] / ceil, 4)}
+    for tag, r in (("16k", r16), ("8k", r8k)):
+        if r:
+            for bud, x in r.items():
+                vs_stream[f"draft_{tag}_budget{bud}"] = round(x["draft_gbs"] / ceil, 4)
+            vs_stream[f"tree_verify_{tag}"] = round(r["256"]["verify_gbs"] / ceil, 4)
+            vs_stream[f"accept_{tag}"] = round(r["256"]["accept_gbs"] / ceil, 4)
+    for tree_name in ("tree44", "tree64"):
+        vs_stream[f"ragged_verify_{tree_name}"] = round(rrag[tree_name]["verify_gbs"] / ceil, 4)
+    floor = probes["read_16_8mb_floor_us"]
+    draft_floor = {"read_16_8mb_floor_us": floor,
+                   "empty_launch_us": probes["empty_launch_us"]["256_workgroups"],
+                   "ctx_draft_1m_us": round(r1m["components_ms"]["ctx_draft_per_call"] * 1e3, 2),
+                   "fwd_draft_1m_us": round(r1m["components_ms"]["fwd_draft_per_call"] * 1e3, 2)}
     line = {
         "metric": METRIC,
         "value": round(r1m["gbs"], 2),
@@ -1066,7 +1205,13 @@ def main():
                      "avg_launch_ms": round(v_ms, 4)},
         "cpu_baseline": cpu,
         "roofline_tree_verify_16k": tree_verify_roofline(r16),
+        "roofline_tree_verify_8k": tree_verify_roofline(r8k),
+        "machine": probes,
+        "vs_stream_read": vs_stream,
+        "draft_floor": draft_floor,
+        "verify_modes_1m": r1m["verify_modes"],
         "ctx16k": r16,
+        "ctx8k": r8k,
         "ctx4k": r4k,
         "ragged": rrag,
         "kv_commit": commit,

@@ -29,11 +29,13 @@ __all__ = [
     "AttnCase", "make_attn_case",
     "budget_indices", "Tree", "heap_tree", "chain_tree", "layered_tree",
     "draft_tokens", "plant_acceptance", "AcceptCase",
-    "make_accept_case", "pad_groups", "config_tiny", "config_4k", "config_16k",
+    "make_accept_case", "pad_groups", "config_tiny", "config_4k", "config_8k", "config_16k",
     "config_ragged",
 ]
 
-SEEDS = {1: 1000, 2: 2000, 3: 3000, 4: 4000, 5: 5000}
+# Seed 1000 c for workload c = 1..5; the 8K point between the 4K and 16K
+# workloads (BudgetDraft sweeps its budgets at 4K, 8K and 16K) takes 3500.
+SEEDS = {1: 1000, 2: 2000, 3: 3000, 4: 4000, 5: 5000, "8k": 3500}
 PLANT_LOGIT = 10.0
 
 
@@ -306,6 +308,12 @@ def config_16k(seed: int = SEEDS[3], budgets=(256, 512, 1024, 2048), L: int = 16
            for bud in budgets}
     return dict(case=case, idx=idx, tree=tree, verify_q=vq, tree_k=tk, tree_v=tv,
                 vocab=128256)
+
+
+def config_8k(seed: int = SEEDS["8k"], budgets=(256, 512, 1024, 2048)) -> dict:
+    """8K: the 16K recipe at L = 8192 (batch 8, budgets 256..2048 per
+    sequence, the 64-node tree of widths 10/18/18/18, vocab 128,256)."""
+    return config_16k(seed, budgets, L=8192, B=8)
 
 
 def config_ragged(seed: int = SEEDS[5], widths=(10, 14, 12, 8), B: int = 16,

@@ -360,3 +360,28 @@ def test_binding_fails_loudly_without_library(tmp_path):
             skg._lib.load(str(tmp_path / "missing.so"))
     finally:
         skg._lib._lib = saved
+
+
+PROBE_HEADER = os.path.join(ROOT, "include", "spec_probe.h")
+
+
+def test_probe_library_exports_its_header():
+    """The measurement library loads and exports every function of
+    spec_probe.h; its argument checks reject bad shapes before a launch."""
+    import torch
+    import sparse_kv_attention_sink_amd._probe as pr
+    text = open(PROBE_HEADER).read()
+    fns = sorted(set(re.findall(r"^\s*int32_t\s+(spec_\w+)\(", text, flags=re.M)))
+    assert fns == sorted(pr.EXPORTED)
+    plib = pr.load()
+    for name in fns:
+        assert hasattr(plib, name), name
+    if torch.cuda.is_available():
+        return
+    fake = ctypes.c_void_p(1 << 20)
+    assert plib.spec_probe_read(fake, 4096 * 3 + 1, 8, 8, fake, None) == -1   # not whole blocks
+    assert plib.spec_probe_read(fake, 4096, 8, 5, fake, None) == -1           # in_flight
+    assert plib.spec_probe_read(None, 4096, 8, 8, fake, None) == -1
+    assert plib.spec_probe_read_lds(fake, 16384, 8, 3, fake, None) == -1      # stages
+    assert plib.spec_probe_read_lds(fake, 4096, 8, 4, fake, None) == -1      # not whole stages
+    assert plib.spec_probe_empty(0, fake, None) == -1

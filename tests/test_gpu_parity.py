@@ -162,6 +162,48 @@ def test_16k_accept(c16k):
     np.testing.assert_array_equal(got[0], a.expected_len)
 
 
+# ------------------------------------------------------------ 8K workload
+
+@pytest.fixture(scope="module")
+def c8k():
+    return synth.config_8k()
+
+
+@pytest.mark.parametrize("budget", [256, 512, 1024, 2048])
+def test_8k_draft_budget_sweep(c8k, budget):
+    case = c8k["case"]
+    idx = c8k["idx"][budget]
+    got, lse = run_draft(case, idx=idx)
+    ref, lse_ref = oracle.draft_attn_ref(case.q, case.k, case.v, case.cache_len, scale=case.scale,
+                                         idx=idx)
+    assert_close(got, ref, "bf16", f"8K draft B={budget}")
+    assert_lse_close(lse, lse_ref, 1e-3, "8K draft lse")
+
+
+def test_8k_verify_64_node_tree_sampled(c8k):
+    """Full-size launch; the oracle checks every row of three (sequence,
+    KV head) pairs."""
+    case, tree = c8k["case"], c8k["tree"]
+    got, lse, pos = run_verify(case, c8k["verify_q"], c8k["tree_k"], c8k["tree_v"], tree.parents)
+    pairs = [(1, 2), (4, 0), (6, 7)]
+    ref, lse_ref = oracle.verify_attn_ref(c8k["verify_q"], case.k, case.v, case.cache_len,
+                                          c8k["tree_k"], c8k["tree_v"], tree.parents,
+                                          scale=case.scale, pairs=pairs)
+    assert_close(got, ref, "bf16", "8K verify")
+    assert_lse_close(lse, lse_ref, 1e-3, "8K verify lse")
+    assert np.all(np.isfinite(got))
+    np.testing.assert_array_equal(pos, oracle.position_ids(case.cache_len, None, tree.parents))
+
+
+def test_8k_accept(c8k):
+    a = synth.make_accept_case(synth.SEEDS["8k"] + 1, c8k["tree"], 8, 128256)
+    got = run_accept(a)
+    ref = oracle.accept_ref(a.logits, a.tokens, a.parents, a.max_depth)
+    for g, r in zip(got, ref):
+        np.testing.assert_array_equal(g, r)
+    np.testing.assert_array_equal(got[0], a.expected_len)
+
+
 # ------------------------------------------------------------ small ragged shapes
 
 SHAPES = [
