@@ -385,7 +385,7 @@ def run_ctx(args, torch, skg, L, seed):
         db = draft_bytes(Bsz, L, 1, bud) + Bsz * bud * 4
         ab = accept_bytes(Bsz, N, VOCAB)
         out[str(bud)] = dict(
-            graph_ms_step=g_ms, graph_steps_per_s=1e3 / g_ms,
+            context=L, graph_ms_step=g_ms, graph_steps_per_s=1e3 / g_ms,
             ms_step=ms_step, steps_per_s=1e3 / ms_step,
             gbs=(vb + 4 * db + ab) / (ms_step * 1e-3) / 1e9,
             t_verify_ms=tv_ms, t_draft_ms=td_ms, t_accept_ms=ta_ms,
@@ -440,8 +440,8 @@ def run_probes(torch):
         return a.elapsed_time(b) / reps
 
     shapes = {}
-    for wg in (1024, 2048, 4096, 8192):
-        for inf in (4, 8, 16):
+    for wg in (2048, 4096, 8192, 16384, 32768, 65536):
+        for inf in (8, 16):
             ms = timed(lambda: pr.read(buf, wg, inf, sink))
             shapes[f"regs_wg{wg}_inflight{inf}"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
     for wg in (256, 512):
@@ -485,7 +485,7 @@ def tree_verify_roofline(r16):
         return None
     r = r16["256"]
     tf = r["verify_tflops"]
-    return {"kernel": "tree verify (64 nodes x GQA 4, batch 8 x 16,384 keys)", "bound": "hbm",
+    return {"kernel": f"tree verify (64 nodes x GQA 4, batch 8 x {r['context']:,} keys)", "bound": "hbm",
             "achieved": round(r["verify_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(r["verify_gbs"] / HBM_PEAK_GBS, 4),
             "mfma_tflops": round(tf, 1), "mfma_peak_tflops": 2500.0, "mfma_frac": round(tf / 2500.0, 4),

@@ -88,6 +88,7 @@ Plan bf16_plan(const spec_dims* d, int32_t T, int64_t tiles, bool gather, bool v
   Plan p;
   const int G = d->n_q_heads / d->n_kv_heads;
   const int64_t pairs = (int64_t)d->batch * d->n_kv_heads;
+  if ((int64_t)T * G > kMaxRows) return p;   // total 0: refused
   p.rows = T * G;
   if (p.rows <= 32) {           // few rows: four private rings per workgroup
     p.wk = 4;
@@ -196,6 +197,7 @@ Plan f32_plan(const spec_dims* d, int32_t T, int64_t keys, bool verify) {
   Plan p;
   const int G = d->n_q_heads / d->n_kv_heads;
   const int64_t pairs = (int64_t)d->batch * d->n_kv_heads;
+  if ((int64_t)T * G > kMaxRows) return p;   // total 0: refused
   p.rows = T * G;
   p.rb = 1;
   p.n_rb = p.rows;
@@ -895,6 +897,74 @@ spec_status spec_device_status(void* workspace, void* stream, uint32_t* bits_or_
   if (e != hipSuccess) return hip_fail(e, "hipMemcpy (clear error word)");
   return fail(SPEC_E_DEVICE_RANGE, "device range error bits 0x%x", bits);
 }
+
+#ifdef SPEC_DEBUG_PLAN
+// Debug build only: walks every workgroup of the bf16 attention plan of a
+// shape, the way the kernel derives its ranges, and checks that what the
+// kernel stages and addresses stays inside its LDS arrays, its counters and
+// the workspace.  mode: 0 window draft, 1 budget draft, 2 verify; `extent`
+// is the view length (drafts) or the cache capacity (verify).  Returns 0
+// (in bounds), 1 (shape refused, nothing to check) or -1 with a message.
+int32_t spec_debug_check_plan(const spec_dims* d, int32_t mode, int32_t T, int64_t extent,
+                              char* msg, size_t msg_len) {
+  auto bad = [&](const char* fmt, auto... args) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Wformat-security"
+    snprintf(msg, msg_len, fmt, args...);
+#pragma clang diagnostic pop
+    return (int32_t)-1;
+  };
+  if (check_dims(d) != SPEC_OK || d->dtype != SPEC_BF16 || T < 1 || extent < 0) return 1;
+  if (mode == 2 && T > kMaxNodes) return 1;
+  const bool gather = mode == 1, verify = mode == 2;
+  const int64_t tiles = verify ? cdiv(extent, kTileKeys) + cdiv(T, kTileKeys)
+                               : cdiv(std::max<int64_t>(extent, 1), kTileKeys);
+  if (tiles > INT32_MAX / 2) return 1;
+  const Plan p = verify ? verify_plan(d, T, (int32_t)std::min<int64_t>(extent, INT32_MAX))
+                        : draft_plan(d, T, extent, gather);
+  if (p.total == 0) return 1;
+  const int G = d->n_q_heads / d->n_kv_heads;
+  const int64_t pairs = (int64_t)d->batch * d->n_kv_heads;
+  const int64_t groups = pairs * p.n_rb;
+  if ((int64_t)p.rb * p.n_rb < (int64_t)T * G) return bad("row blocks %d x %d miss rows %d", p.n_rb, p.rb, T * G);
+  if (p.rb != (p.wk == 4 ? 16 * p.rt : 64 * p.rt)) return bad("row block %d does not match the shape", p.rb);
+  if ((int64_t)p.splits * p.tps < tiles || (int64_t)(p.splits - 1) * p.tps >= tiles)
+    return bad("splits %d x %d tiles do not cover %lld tiles exactly", p.splits, p.tps, (long long)tiles);
+  if (p.splits > kMaxSplits || p.n_blk != cdiv(p.splits, kMergeFan)) return bad("merge plan");
+  if (verify && p.ordered && d->batch > kMaxOrderBatch) return bad("ordered verify beyond %d", kMaxOrderBatch);
+  // counters: [cnt_l0: groups x n_blk][cnt_l1: groups][cnt_pos: 2B][cnt_chunk: groups]
+  const int64_t words = groups * p.n_blk + groups + 2 * (int64_t)d->batch + groups;
+  if (p.cnt_off != kHeaderBytes || words > (int64_t)kCounterWords)
+    return bad("%lld counter words exceed the region", (long long)words);
+  if (p.splits > 1) {
+    const uint64_t part = (uint64_t)p.splits * p.rb * d->head_dim * 4;   // one group's o partials
+    if (part > UINT32_MAX) return bad("a group's partials exceed a buffer descriptor");
+    if (p.o_off < kScratchOff || p.o_off + groups * part > p.lse_off ||
+        p.lse_off + (uint64_t)groups * p.splits * p.rb * 4 > (p.n_blk > 1 ? p.o1_off : p.total))
+      return bad("split partials overlap");
+  }
+  if (p.n_blk > 1 && p.lse1_off + (uint64_t)groups * p.n_blk * p.rb * 4 > p.total)
+    return bad("block partials overrun the workspace");
+  const int64_t cache_tiles_max = verify ? cdiv(extent, kTileKeys) : tiles;
+  for (int s = 0; s < p.splits; ++s) {
+    // the largest total a workgroup can meet is the plan's own bound
+    int t0, t1;
+    split_tiles((int)tiles, p.tps, s, t0, t1);
+    if (t0 > t1) return bad("split %d: empty range reversed", s);
+    if (gather) {
+      const int64_t cnt = std::max<int64_t>(0, std::min<int64_t>((int64_t)t1 * kTileKeys, extent) -
+                                                   (int64_t)t0 * kTileKeys);
+      if (cnt > kMaxGatherKeys) return bad("split %d stages %lld budget indices", s, (long long)cnt);
+    }
+    if (verify) {
+      const int64_t wend = std::min<int64_t>(t1, cache_tiles_max);
+      if (wend - t0 > kMaxPadWords) return bad("split %d stages %lld pad words", s, (long long)(wend - t0));
+    }
+  }
+  if (grid_size(d, p) > kMaxGrid) return bad("grid");
+  return 0;
+}
+#endif
 
 }  // extern "C"
 #pragma GCC visibility pop

@@ -454,8 +454,8 @@ void attn_bf16_kernel(AttnArgs a) {
   const int cache_tiles = (n_view + kTileKeys - 1) / kTileKeys;
   const int tree_tiles = (MODE == kVerify && !bad) ? (N + kTileKeys - 1) / kTileKeys : 0;
   const int total = cache_tiles + tree_tiles;
-  const int t0 = min(total, s * a.tps);
-  const int t1 = min(total, t0 + a.tps);
+  int t0, t1;
+  split_tiles(total, a.tps, s, t0, t1);
   int k0 = t0, k1 = t1;
   if constexpr (WK == 4) {
     const int per = (t1 - t0 + 3) / 4;

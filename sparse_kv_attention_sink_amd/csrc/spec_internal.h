@@ -45,6 +45,7 @@ constexpr int kCompactSlices = 64;             // pad-scan workgroups per sequen
 constexpr int kCompactScanSlots = 65536;       // compaction: longer pad rows are scanned in slices
 constexpr int kMaxSelectBlocks = 8192;         // candidate blocks one selection scores
 constexpr int kMaxSelect = 2048;               // blocks one selection may choose
+constexpr int kMaxRows = 1 << 16;              // query rows (tokens x GQA group) per (sequence, KV head)
 
 enum Mode : int { kDraftWindow = 0, kDraftGather = 1, kVerify = 2 };
 
@@ -110,6 +111,14 @@ struct Plan {
 };
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Tiles [t0, t1) of split s when a (sequence, KV head) has `total` tiles and
+// every split takes `tps` (the attention kernel and the host-side plan
+// checker of the debug build compute it the same way).
+__host__ __device__ inline void split_tiles(int total, int tps, int s, int& t0, int& t1) {
+  t0 = s * tps < total ? s * tps : total;
+  t1 = t0 + tps < total ? t0 + tps : total;
+}
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Arguments of the KV commit kernel (byte strides; validated by the caller).
