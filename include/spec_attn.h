@@ -242,6 +242,32 @@ spec_status spec_attn_verify_tree(const spec_dims* dims, const void* q, int32_t 
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the tree
+ * verify of spec_attn_verify_tree, same arguments, same kernels and the
+ * same results, but without a workspace argument.  Its scratch (the
+ * workspace layout: error word, counters, split partials) is a static
+ * device array of 64 MiB in the library, one copy per GPU, held from the
+ * first call on that GPU until the process ends.  A shape whose workspace
+ * (spec_verify_workspace_bytes) exceeds 64 MiB returns SPEC_E_UNSUPPORTED
+ * before anything is launched.  The call allocates nothing: no hipMalloc,
+ * hipFree or allocating library routine, on the first call or later.
+ *
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (two streams, or two threads) race and must not be issued.
+ * The stream must belong to the current device.  Device range errors poison
+ * the outputs as in spec_attn_verify_tree; the static error word is not
+ * reported (spec_device_status needs a caller workspace).
+ */
+spec_status spec_attn_verify_tree_noalloc(const spec_dims* dims, const void* q, int32_t n_nodes,
+                                          const spec_kv* cache, const int32_t* cache_len,
+                                          const uint8_t* pad_or_null, int64_t pad_stride_b,
+                                          const spec_kv* tree, const int32_t* parents,
+                                          int64_t parents_stride_b, void* out,
+                                          float* lse_or_null, int32_t* pos_ids_or_null,
+                                          void* stream);
+
+/*
  * Greedy tree acceptance ([BD] Figure 2; [WM] losslessness; [PV] 4.1).
  *
  * logits fp32 [B][N+1][V] contiguous, 16-byte aligned: row 0 is the

@@ -11,7 +11,7 @@ from ._lib import (  # noqa: F401
     accept_workspace_bytes, commit_workspace_bytes, compact_workspace_bytes, draft_workspace_bytes,
     load, make_dims,
     new_workspace, spec_accept_greedy, spec_attn_draft_ring, spec_attn_draft_sparse,
-    spec_attn_verify_tree, spec_kv_compact,
+    spec_attn_verify_tree, spec_attn_verify_tree_noalloc, spec_kv_compact,
     SPEC_VERIFY_FULL, SPEC_VERIFY_PARTIAL, spec_block_means, spec_device_status, spec_kv_commit,
     spec_kv_gather, spec_select_blocks, spec_verify_mode, select_workspace_bytes,
     verify_workspace_bytes,

@@ -38,6 +38,7 @@ EXPORTED = [
     "spec_attn_draft_sparse", "spec_attn_draft_ring", "spec_attn_verify_tree",
     "spec_accept_greedy", "spec_kv_commit", "spec_kv_compact", "spec_compact_workspace_bytes",
     "spec_draft_workspace_bytes", "spec_verify_workspace_bytes", "spec_accept_workspace_bytes",
+    "spec_attn_verify_tree_noalloc",
     "spec_commit_workspace_bytes", "spec_block_means", "spec_select_blocks",
     "spec_select_workspace_bytes", "spec_kv_gather", "spec_verify_mode",
     "spec_device_status", "spec_status_string", "spec_last_error", "spec_abi_version",
@@ -82,6 +83,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.spec_attn_draft_ring.restype = I32
     lib.spec_attn_verify_tree.argtypes = [P, P, I32, P, P, P, I64, P, P, I64, P, P, P, P, SZ, P]
     lib.spec_attn_verify_tree.restype = I32
+    lib.spec_attn_verify_tree_noalloc.argtypes = [P, P, I32, P, P, P, I64, P, P, I64, P, P, P, P]
+    lib.spec_attn_verify_tree_noalloc.restype = I32
     lib.spec_accept_greedy.argtypes = [I32, I32, I32, P, P, P, I64, I32, P, P, P, P, SZ, P]
     lib.spec_accept_greedy.restype = I32
     lib.spec_kv_commit.argtypes = [I32, I32, I32, I32, P, P, P, I64, P, I32, P, P, I32, P, P, SZ, P]
@@ -298,6 +301,34 @@ def spec_attn_verify_tree(q, k_cache, v_cache, cache_len, tree_k, tree_v, parent
                                    _ptr(cache_len), _ptr(pad), pad_sb, ctypes.byref(tkv),
                                    _ptr(parents), psb, _ptr(out), _ptr(lse), _ptr(pos_ids),
                                    _ptr(workspace), workspace.numel(), _stream(q))
+    _check(st)
+    return out, lse, pos_ids
+
+
+def spec_attn_verify_tree_noalloc(q, k_cache, v_cache, cache_len, tree_k, tree_v, parents, *,
+                                  out, pos_ids=None, lse=None, pad=None, scale=None,
+                                  deterministic=False):
+    """spec_attn_verify_tree on the library's static scratch: no workspace,
+    and the caller passes every output it wants (``out`` is required), so the
+    call allocates nothing.  Returns (out, lse, pos_ids)."""
+    lib = load()
+    _on_gpu(q, k_cache, v_cache, cache_len, tree_k, tree_v, parents, pad, out, lse, pos_ids)
+    if q.dim() != 4 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B, N, Hq, D] tensor")
+    B, N, Hq, D = q.shape
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped and typed like q")
+    if parents.dtype != torch.int32 or parents.shape[-1] != N or parents.stride(-1) != 1:
+        raise ValueError("parents must be int32 [N] or [B, N]")
+    psb = 0 if parents.dim() == 1 else parents.stride(0)
+    kv = _kv(k_cache, v_cache)
+    tkv = _kv(tree_k, tree_v)
+    dims = make_dims(B, Hq, k_cache.shape[1], D, _dtype_code(q), scale, deterministic)
+    pad_sb = 0 if pad is None else pad.stride(0)
+    st = lib.spec_attn_verify_tree_noalloc(ctypes.byref(dims), _ptr(q), N, ctypes.byref(kv),
+                                           _ptr(cache_len), _ptr(pad), pad_sb, ctypes.byref(tkv),
+                                           _ptr(parents), psb, _ptr(out), _ptr(lse), _ptr(pos_ids),
+                                           _stream(q))
     _check(st)
     return out, lse, pos_ids
 

@@ -17,7 +17,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libspecattn.so")
-SOURCES = ["api.hip", "attn.hip", "generic.hip", "accept.hip", "commit.hip", "select.hip", "gather.hip"]
+SOURCES = ["api.hip", "attn.hip", "generic.hip", "accept.hip", "commit.hip", "select.hip", "gather.hip",
+           "noalloc.hip"]
 # measurement kernels (HBM read ceiling, launch floor), a library of their own
 PROBE_LIB = os.path.join(PKG, "libspecprobe.so")
 PROBE_SOURCES = ["probe.hip"]

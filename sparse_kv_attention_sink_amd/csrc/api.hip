@@ -294,6 +294,8 @@ void fill_plan(AttnArgs& a, const Plan& p, void* workspace) {
 
 }  // namespace
 
+spec_status spec::set_error(spec_status s, const char* msg) { return fail(s, "%s", msg); }
+
 #pragma GCC visibility push(default)
 extern "C" {
 
@@ -459,6 +461,26 @@ spec_status spec_attn_verify_tree(const spec_dims* dims, const void* q, int32_t 
                                   int64_t parents_stride_b, void* out, float* lse_or_null,
                                   int32_t* pos_ids_or_null, void* workspace,
                                   size_t workspace_bytes, void* stream) {
+  return spec::verify_impl(dims, q, n_nodes, cache, cache_len, pad_or_null, pad_stride_b, tree,
+                           parents, parents_stride_b, out, lse_or_null, pos_ids_or_null,
+                           workspace, workspace_bytes, stream, nullptr);
+}
+
+}  // extern "C"
+
+// Validation, planning and launches of the tree verify.  With `need` set,
+// the workspace bytes the call requires are stored there once the
+// arguments are known to be valid, and nothing is launched if the
+// workspace is NULL (the static-workspace variant asks first).
+__attribute__((visibility("hidden")))
+spec_status spec::verify_impl(const spec_dims* dims, const void* q, int32_t n_nodes,
+                              const spec_kv* cache, const int32_t* cache_len,
+                              const uint8_t* pad_or_null, int64_t pad_stride_b,
+                              const spec_kv* tree, const int32_t* parents,
+                              int64_t parents_stride_b, void* out, float* lse_or_null,
+                              int32_t* pos_ids_or_null, void* workspace, size_t workspace_bytes,
+                              void* stream, size_t* need) {
+  if (need != nullptr) *need = 0;
   spec_status st = check_dims(dims);
   if (st != SPEC_OK) return st;
   if (n_nodes < 1 || n_nodes > kMaxNodes)
@@ -481,11 +503,15 @@ spec_status spec_attn_verify_tree(const spec_dims* dims, const void* q, int32_t 
   }
   const Plan p = verify_plan(dims, n_nodes, cache->capacity);
   if (p.total == 0) return fail(SPEC_E_UNSUPPORTED, "no split plan fits this shape");
+  if (grid_size(dims, p) > kMaxGrid) return fail(SPEC_E_UNSUPPORTED, "problem too large for one launch");
+  if (need != nullptr) {
+    *need = p.total;
+    if (workspace == nullptr) return SPEC_OK;
+  }
   if (workspace == nullptr || workspace_bytes < p.total)
     return fail(SPEC_E_WORKSPACE, "workspace of %zu bytes needed (got %zu)", p.total,
                 workspace == nullptr ? (size_t)0 : workspace_bytes);
   if (!aligned(workspace, 256)) return fail(SPEC_E_INVALID, "workspace must be 256-byte aligned");
-  if (grid_size(dims, p) > kMaxGrid) return fail(SPEC_E_UNSUPPORTED, "problem too large for one launch");
 
   AttnArgs a{};
   a.q = q;
@@ -537,6 +563,8 @@ spec_status spec_attn_verify_tree(const spec_dims* dims, const void* q, int32_t 
   }
   return SPEC_OK;
 }
+
+extern "C" {
 
 spec_status spec_accept_greedy(int32_t batch, int32_t n_nodes, int32_t vocab, const float* logits,
                                const int32_t* draft_tokens, const int32_t* parents,

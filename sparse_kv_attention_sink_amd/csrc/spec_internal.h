@@ -198,6 +198,19 @@ struct GatherArgs {
   uint32_t* err;
 };
 
+// The tree verify behind spec_attn_verify_tree: validation, planning and
+// launches.  With need != NULL the required workspace bytes are stored
+// there once the arguments are valid, and a NULL workspace launches nothing.
+spec_status verify_impl(const spec_dims* dims, const void* q, int32_t n_nodes,
+                        const spec_kv* cache, const int32_t* cache_len,
+                        const uint8_t* pad_or_null, int64_t pad_stride_b, const spec_kv* tree,
+                        const int32_t* parents, int64_t parents_stride_b, void* out,
+                        float* lse_or_null, int32_t* pos_ids_or_null, void* workspace,
+                        size_t workspace_bytes, void* stream, size_t* need);
+
+// Sets the thread-local message of spec_last_error() and returns `s`.
+spec_status set_error(spec_status s, const char* msg);
+
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error; arguments were validated.
 hipError_t launch_attn_bf16(const AttnArgs& a, int mode, const Plan& p, hipStream_t st);

@@ -385,3 +385,31 @@ def test_probe_library_exports_its_header():
     assert plib.spec_probe_read_lds(fake, 16384, 8, 3, fake, None) == -1      # stages
     assert plib.spec_probe_read_lds(fake, 4096, 8, 4, fake, None) == -1      # not whole stages
     assert plib.spec_probe_empty(0, fake, None) == -1
+
+
+def test_noalloc_verify_refuses_shapes_beyond_its_static_scratch(lib):
+    """The static scratch holds 64 MiB: a shape needing more is refused
+    before anything is launched; invalid arguments fail as in the workspace
+    variant; batch 0 is a no-op."""
+    d = dims(B=256)
+    assert skg.verify_workspace_bytes(d, 64, 1 << 17) > 64 << 20
+    fake = 1 << 20
+    kv = SpecKV(fake, fake, 8 * (1 << 17) * 128, (1 << 17) * 128, 128, 1 << 17)
+    tr = SpecKV(fake, fake, 8 * 64 * 128, 64 * 128, 128, 64)
+    P = ctypes.c_void_p
+    st = lib.spec_attn_verify_tree_noalloc(ctypes.byref(d), P(fake), 64, ctypes.byref(kv), P(fake),
+                                           None, 0, ctypes.byref(tr), P(fake), 0, P(fake), None, None,
+                                           None)
+    assert st == skg.SPEC_E_UNSUPPORTED
+    assert b"static array" in lib.spec_last_error()
+    st = lib.spec_attn_verify_tree_noalloc(ctypes.byref(d), P(fake), 65, ctypes.byref(kv), P(fake),
+                                           None, 0, ctypes.byref(tr), P(fake), 0, P(fake), None, None,
+                                           None)
+    assert st == skg.SPEC_E_UNSUPPORTED          # more than 64 nodes
+    st = lib.spec_attn_verify_tree_noalloc(ctypes.byref(d), None, 64, ctypes.byref(kv), P(fake),
+                                           None, 0, ctypes.byref(tr), P(fake), 0, P(fake), None, None,
+                                           None)
+    assert st == skg.SPEC_E_INVALID              # null q
+    z = dims(B=0)
+    assert lib.spec_attn_verify_tree_noalloc(ctypes.byref(z), None, 5, None, None, None, 0, None,
+                                             None, 0, None, None, None, None) == skg.SPEC_OK
