@@ -647,7 +647,7 @@ void attn_bf16_kernel(AttnArgs a) {
       if (k0 + u < k1) issue(k0 + u, u);
   }
   // Register-staged splits (WK = 4) of long key ranges: each wave streams a
-  // fixed run of about three quarters of its share, then takes chunks of
+  // fixed run of about seven eighths of its share, then takes chunks of
   // a.dyn tiles from a pool shared by the (pair, row block) through an
   // arrival-style counter, so that waves on faster XCDs take over work of
   // slower ones.  A wave requests its next chunk right after issuing the
@@ -658,7 +658,7 @@ void attn_bf16_kernel(AttnArgs a) {
   const int C = dyn ? a.dyn : 1;
   const int n_chunks = (total + C - 1) / C;
   const int wpp = a.splits * 4;                       // waves per (pair, row block)
-  const int F = dyn ? (n_chunks * 3 / 4) / wpp : 0;   // fixed chunks per wave
+  const int F = dyn ? (n_chunks * 7 / 8) / wpp : 0;   // fixed chunks per wave
   const int pool0 = wpp * F;                          // first pooled chunk
   int t_first = k0 < k1 ? k0 : -1, run_end = k1, c_next = 0;
   bool pending = false;   // a pool request is on its way
