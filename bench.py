@@ -1094,6 +1094,8 @@ def main():
     ap.add_argument("--skip-1m", action="store_true",
                     help="only the 16K batch-8 sweep (for profiling it alone)")
     ap.add_argument("--skip-cpu", action="store_true")
+    ap.add_argument("--ragged-only", action="store_true",
+                    help="only the ragged batch of 16 (for profiling it alone)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 1 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -1109,6 +1111,9 @@ def main():
         copy_probe(torch)
         return
 
+    if args.ragged_only:
+        print(json.dumps({"ragged": run_ragged(args, torch, skg)}), flush=True)
+        return
     if args.skip_1m:
         print(json.dumps({"ctx16k": run_16k(args, torch, skg),
                           "ctx8k": run_8k(args, torch, skg)}), flush=True)
