@@ -234,33 +234,34 @@ __device__ __forceinline__ void store_tile_lds(uint32_t stage, int lane, const u
   }
 }
 
-// Merge n (1..kMergeFan) partial results of RC rows: partial p of row rl is
-// o (normalised by its own softmax sum) at o_rs[((p0 + p) * RC + rl) * D + d]
+// Merge n (1..P) partial results of RC rows: partial p of row rl is o
+// (normalised by its own softmax sum) at o_rs[((p0 + p) * RC + rl) * D + d]
 // and its log2 sum-exp at l_rs[(p0 + p) * RC + rl].  For every (row, 4 head-
-// dim values) item of the first `rows` rows, all loads are issued before any
-// is used, two items at a time (partials past n re-read the last one and get
-// weight 0), and
-// sink(rl, d0, o[4], lse2) receives sum_p 2^(x_p - M) o_p / sum_p 2^(x_p - M)
+// dim values) item of the first `rows` rows, the loads of U items are issued
+// before any is used (partials past n re-read the last one and get weight 0),
+// and sink(rl, d0, o[4], lse2) receives sum_p 2^(x_p - M) o_p / sum_p 2^(x_p - M)
 // and M + log2 sum_p 2^(x_p - M), M = max_p x_p: NaN if any partial is NaN,
 // o = 0 and lse = -inf if every partial is empty.
-template <int D, int RC, typename Sink>
-__device__ __forceinline__ void merge_partials(__amdgpu_buffer_rsrc_t o_rs, __amdgpu_buffer_rsrc_t l_rs,
-                                               int p0, int n, int rows, Sink sink) {
+template <int D, int RC, int P, typename Sink>
+__device__ __forceinline__ void merge_partials_p(__amdgpu_buffer_rsrc_t o_rs, __amdgpu_buffer_rsrc_t l_rs,
+                                                 int p0, int n, int rows, Sink sink) {
   constexpr int kItems = RC * (D / 4);
   constexpr int kPerThread = (kItems + 255) / 256;
-  // items whose loads are in flight together (one for D = 64, where the
-  // registers of a second item would cost the main loop occupancy)
-  constexpr int U = (kPerThread >= 2 && D == 128) ? 2 : 1;
+  // about 32 partial loads in flight per thread at D = 128, 16 at D = 64
+  // (where more registers would cost the main loop occupancy)
+  constexpr int kLoads = D == 128 ? 32 : 16;
+  constexpr int Uw = kLoads / P > 0 ? kLoads / P : 1;
+  constexpr int U = Uw < kPerThread ? Uw : kPerThread;
   for (int i0 = 0; i0 < kPerThread; i0 += U) {
-    float x[U][kMergeFan];
-    f32x4 ov[U][kMergeFan];
+    float x[U][P];
+    f32x4 ov[U][P];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int it = (int)threadIdx.x + (i0 + u) * 256;
       const int rl = it / (D / 4), d0 = (it % (D / 4)) * 4;
       const bool live = it < kItems && rl < rows;
 #pragma unroll
-      for (int p = 0; p < kMergeFan; ++p) {
+      for (int p = 0; p < P; ++p) {
         const int pp = p0 + min(p, n - 1);
         // a dead item reads row 0 of the first partial (always in range)
         const int r = live ? rl : 0, dd = live ? d0 : 0;
@@ -276,7 +277,7 @@ __device__ __forceinline__ void merge_partials(__amdgpu_buffer_rsrc_t o_rs, __am
       float M = -INFINITY;
       bool nan = false;
 #pragma unroll
-      for (int p = 0; p < kMergeFan; ++p)
+      for (int p = 0; p < P; ++p)
         if (p < n) {
           nan |= isnan(x[u][p]);
           M = fmaxf(M, x[u][p]);
@@ -284,7 +285,7 @@ __device__ __forceinline__ void merge_partials(__amdgpu_buffer_rsrc_t o_rs, __am
       float W = 0.f, o[4] = {0.f, 0.f, 0.f, 0.f};
       if (!nan && M != -INFINITY) {
 #pragma unroll
-        for (int p = 0; p < kMergeFan; ++p) {
+        for (int p = 0; p < P; ++p) {
           const float f = p < n ? __builtin_amdgcn_exp2f(x[u][p] - M) : 0.f;
           W += f;
 #pragma unroll
@@ -309,6 +310,17 @@ __device__ __forceinline__ void merge_partials(__amdgpu_buffer_rsrc_t o_rs, __am
       sink(rl, d0, o, lse2);
     }
   }
+}
+
+// Merge n (1..kMergeFan) partials, loading only as many as there are, to the
+// next multiple of 4: most tree verifies merge 4 or fewer.
+template <int D, int RC, typename Sink>
+__device__ __forceinline__ void merge_partials(__amdgpu_buffer_rsrc_t o_rs, __amdgpu_buffer_rsrc_t l_rs,
+                                               int p0, int n, int rows, Sink sink) {
+  static_assert(kMergeFan == 16, "merge widths 4, 8 and 16");
+  if (n <= 4) merge_partials_p<D, RC, 4>(o_rs, l_rs, p0, n, rows, sink);
+  else if (n <= 8) merge_partials_p<D, RC, 8>(o_rs, l_rs, p0, n, rows, sink);
+  else merge_partials_p<D, RC, 16>(o_rs, l_rs, p0, n, rows, sink);
 }
 
 template <int MODE, int D, int RT, int WK, int NS>
