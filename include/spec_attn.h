@@ -56,7 +56,8 @@
  *   - head_dim must be 64 or 128.  Query head h reads KV head h / (Hq / Hkv).
  *   - Size limits of the bf16 path (SPEC_E_UNSUPPORTED beyond them): a
  *     draft budget of at most 524288 positions; a verify cache capacity plus
- *     N of at most 2^23 slots.
+ *     N of at most 2^23 slots; at most 65536 query rows (tokens x query
+ *     heads per KV head) per sequence and KV head.
  *
  * Sources (page title, then the passage):
  *   [WM] "Windowed-MTP: Removing the Full-Context Draft-KV Tax at Million-Token

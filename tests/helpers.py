@@ -32,7 +32,8 @@ def host64(t: torch.Tensor) -> np.ndarray:
 # term covers the two roundings whose error grows with the output itself:
 # the bf16 output (half an ulp, 2^-8 |o|) and the bf16 probabilities of the
 # P.V product (2^-8 of each term, i.e. up to 2^-8 |o| when one key dominates
-# the row).  The absolute 1e-2 is the spec bar; fp32 stays absolute.
+# the row).  The absolute 1e-2 is the bar the workloads state for bf16;
+# fp32 stays absolute.
 RTOL_ELEM = {"bf16": 2.0 ** -7, "f32": 0.0}
 
 # (label, max |err|, fraction of the per-element bar used) of every

@@ -51,3 +51,23 @@ def test_shapes_and_as_f64():
     assert np.array_equal(oracle.as_f64(bits), got)
     f = np.array([1.5, -2.25, 1e-30], dtype=np.float32)
     assert np.array_equal(oracle.as_f64(f), f.astype(np.float64))
+
+
+def test_generator_encoding_round_trips_like_torch():
+    """The generators' float32 -> bf16 rounding (nearest, ties to even) and
+    the oracle's decoding, end to end, against torch's own conversion: ties
+    in both directions, values that carry into the exponent, the largest
+    finite values and overflow to infinity."""
+    import synth
+    rng = np.random.default_rng(7)
+    x = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32) * np.float32(3.0),
+        np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8),   # ties: to even
+                  1.0 + 2.0 ** -8 + 2.0 ** -20, 2.0 - 2.0 ** -9,               # above a tie; carry
+                  3.3895e38, -3.3895e38, 3.4e38, 1e-40, -0.0, 0.0],
+                 dtype=np.float32),
+    ])
+    got = oracle.decode_bf16(synth.round_to_bf16_bits(x))
+    want = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(got, want)
+    assert np.array_equal(np.signbit(got), np.signbit(want))
