@@ -28,11 +28,13 @@ def _normal_bf16(shape, gen, device, scale):
 
 
 def layer_1m(layer: int, *, L: int = L_1M, Hq: int = 32, Hkv: int = 8, D: int = 128,
-             n_chain: int = 3, device="cuda", seed: int = SEEDS[4]) -> dict:
+             n_chain: int = 3, device="cuda", seed: int = SEEDS[4],
+             value_scale: float | None = None) -> dict:
     """Cache K/V ``[1, Hkv, L, D]``, the verify queries of a 3-token chain,
-    its tree K/V, the 3 chained draft queries and 3 single draft queries."""
+    its tree K/V, the 3 chained draft queries and 3 single draft queries;
+    every draw N(0,1)/sqrt(D), or N(0,1) times ``value_scale``."""
     import torch
-    s = 1.0 / math.sqrt(D)
+    s = 1.0 / math.sqrt(D) if value_scale is None else value_scale
     gen = torch.Generator(device=device)
     gen.manual_seed(seed + layer)
     k = torch.empty((1, Hkv, L, D), dtype=torch.bfloat16, device=device)

@@ -277,10 +277,11 @@ def config_tiny(seed: int = SEEDS[1]) -> dict:
                 tree_k=tk, tree_v=tv, vocab=1000)
 
 
-def config_4k(seed: int = SEEDS[2]) -> dict:
-    """4K: B=1, Hq=32, Hkv=8, D=128, bf16 N(0,1)/sqrt(128); draft over a
-    budget of 256 (sink 4, last 128, 124 uniform middle); verify chain of 5."""
-    s = 1.0 / math.sqrt(128)
+def config_4k(seed: int = SEEDS[2], value_scale: float | None = None) -> dict:
+    """4K: B=1, Hq=32, Hkv=8, D=128, bf16 N(0,1)/sqrt(128) (or N(0,1) times
+    ``value_scale``, the peaked variant); draft over a budget of 256 (sink 4,
+    last 128, 124 uniform middle); verify chain of 5."""
+    s = 1.0 / math.sqrt(128) if value_scale is None else value_scale
     case = make_attn_case(seed, B=1, Hq=32, Hkv=8, D=128, L_cap=4096, T=1, value_scale=s)
     rng = case.extra["rng"]
     tree = chain_tree(5)
@@ -293,10 +294,11 @@ def config_4k(seed: int = SEEDS[2]) -> dict:
 
 
 def config_16k(seed: int = SEEDS[3], budgets=(256, 512, 1024, 2048), L: int = 16384,
-               B: int = 8) -> dict:
+               B: int = 8, value_scale: float | None = None) -> dict:
     """16K: B=8, L=16384, budgets 256..2048 drawn per sequence (shared across
-    KV heads), 64-node tree of widths 10/18/18/18 shared across the batch."""
-    s = 1.0 / math.sqrt(128)
+    KV heads), 64-node tree of widths 10/18/18/18 shared across the batch;
+    values N(0,1)/sqrt(128), or N(0,1) times ``value_scale``."""
+    s = 1.0 / math.sqrt(128) if value_scale is None else value_scale
     case = make_attn_case(seed, B=B, Hq=32, Hkv=8, D=128, L_cap=L, T=1, value_scale=s)
     rng = case.extra["rng"]
     tree = layered_tree(rng, (10, 18, 18, 18))

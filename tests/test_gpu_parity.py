@@ -162,6 +162,45 @@ def test_16k_accept(c16k):
     np.testing.assert_array_equal(got[0], a.expected_len)
 
 
+# ------------------------------------------------------------ peaked variants
+# The workloads draw N(0,1)/sqrt(128) values, so their scores spread by about
+# 0.01 and the attention is nearly uniform.  These variants draw queries,
+# keys and values N(0,1) unscaled: scores spread by about 1, the weights are
+# far from uniform, and a masking or rescaling mistake that the near-uniform
+# inputs would average away moves the outputs by far more than the bar.
+
+def test_4k_peaked_draft_and_verify():
+    c = synth.config_4k(value_scale=1.0)
+    case, tree = c["case"], c["tree"]
+    got, lse = run_draft(case, idx=c["idx"])
+    ref, lse_ref = oracle.draft_attn_ref(case.q, case.k, case.v, case.cache_len, scale=case.scale,
+                                         idx=c["idx"])
+    assert_close(got, ref, "bf16", "4K peaked draft")
+    assert_lse_close(lse, lse_ref, 1e-3, "4K peaked draft lse")
+    got, lse, pos = run_verify(case, c["verify_q"], c["tree_k"], c["tree_v"], tree.parents)
+    ref, lse_ref = oracle.verify_attn_ref(c["verify_q"], case.k, case.v, case.cache_len,
+                                          c["tree_k"], c["tree_v"], tree.parents, scale=case.scale)
+    assert_close(got, ref, "bf16", "4K peaked verify")
+    assert_lse_close(lse, lse_ref, 1e-3, "4K peaked verify lse")
+
+
+def test_16k_peaked_draft_and_verify_sampled():
+    c = synth.config_16k(value_scale=1.0, budgets=(1024,))
+    case, tree = c["case"], c["tree"]
+    got, lse = run_draft(case, idx=c["idx"][1024])
+    ref, lse_ref = oracle.draft_attn_ref(case.q, case.k, case.v, case.cache_len, scale=case.scale,
+                                         idx=c["idx"][1024])
+    assert_close(got, ref, "bf16", "16K peaked draft B=1024")
+    assert_lse_close(lse, lse_ref, 1e-3, "16K peaked draft lse")
+    got, lse, pos = run_verify(case, c["verify_q"], c["tree_k"], c["tree_v"], tree.parents)
+    pairs = [(1, 2), (6, 7)]
+    ref, lse_ref = oracle.verify_attn_ref(c["verify_q"], case.k, case.v, case.cache_len,
+                                          c["tree_k"], c["tree_v"], tree.parents,
+                                          scale=case.scale, pairs=pairs)
+    assert_close(got, ref, "bf16", "16K peaked verify")
+    assert_lse_close(lse, lse_ref, 1e-3, "16K peaked verify lse")
+
+
 # ------------------------------------------------------------ 8K workload
 
 @pytest.fixture(scope="module")
