@@ -188,6 +188,42 @@ def test_verify_never_reads_pads_or_slots_past_the_cache():
                                   oracle.position_ids(case.cache_len, pad, tree.parents))
 
 
+@pytest.mark.parametrize("widths", [(3, 5, 4), (10, 18, 18, 18)], ids=["tree12", "tree64"])
+def test_verify_tree_nodes_off_the_ancestor_path_never_leak(widths):
+    """Sentinel tree nodes: every leaf and every other depth-1 node gets a key
+    aligned with the first query of its KV head's group (times 8) and values
+    of +-1000.  A node sees a sentinel only if it is on its own root path, so
+    any sibling, cousin or descendant that leaked into another node's softmax
+    would dominate it; the oracle's outputs (which include the sentinels
+    exactly where the tree says) must be matched on every node."""
+    tree = synth.layered_tree(np.random.default_rng(17), widths)
+    case = small_case(41, T=tree.n)
+    rng = np.random.default_rng(23)
+    tk = synth.draw_normal(rng, (case.B, case.Hkv, tree.n, case.D), 1.0, "bf16")
+    tv = synth.draw_normal(rng, (case.B, case.Hkv, tree.n, case.D), 1.0, "bf16")
+    depth = oracle.tree_depths(tree.parents)
+    leaves = set(range(tree.n)) - set(int(p) for p in tree.parents if p >= 0)
+    sent = sorted(leaves | {i for i in range(tree.n) if depth[i] == 1 and i % 2 == 0})
+    G = case.Hq // case.Hkv
+    for b in range(case.B):
+        for g in range(case.Hkv):
+            qv = oracle.decode_bf16(case.q[b, 0, g * G])
+            tk[b, g, sent] = synth.round_to_bf16_bits((8 * qv).astype(np.float32))
+            tv[b, g, sent] = np.where(np.arange(case.D) % 2 == 0, BF16_1000, BF16_M1000)
+    out, _, _ = skg.spec_attn_verify_tree(dev(case.q), dev(case.k), dev(case.v),
+                                          dev(case.cache_len), dev(tk), dev(tv),
+                                          dev(tree.parents))
+    torch.cuda.synchronize()
+    ref, _ = oracle.verify_attn_ref(case.q, case.k, case.v, case.cache_len, tk, tv,
+                                    tree.parents, scale=case.scale)
+    assert_close(host64(out), ref, "bf16", f"tree sentinel {tree.n} nodes")
+    # the sentinels really dominate where they are visible: a node on whose
+    # path one lies has an output of order 1000 for that head group's first head
+    anc = oracle.tree_ancestors(tree.parents)          # anc[i, j]: j on the root path of i
+    on_path = [i for i in range(tree.n) if anc[i, sent].any()]
+    assert on_path and np.abs(ref[0, on_path, 0]).max() > 100
+
+
 def test_cache_whose_address_has_bit_31_of_its_low_word_set():
     """Regression: the scalar base of a tile copy is rebuilt from two 32-bit
     halves; the low half must not be sign-extended.  K and V are placed
