@@ -912,6 +912,76 @@ def run_ring_1m(torch, skg, layers, *, reps=3):
                 note="per layer: one 3-query context call and three single-query calls")
 
 
+# ------------------------------------------------------------ one GPU's shard
+
+def run_shard_1m(torch, skg, layers, *, reps=3):
+    """One GPU's share of the 1M step under 8-way sharding over KV heads:
+    per layer one KV head (Hkv 1, its 4 query heads) over the same 1,048,576
+    keys, taken as a strided view of the resident layer (layer i uses KV head
+    i mod 8, so the 32 layers' shares do not fit the Infinity Cache): the
+    chain-3 verify and the four draft calls, each timed as a pass over the 32
+    layers with only its bracketing events."""
+    dev = torch.device("cuda:0")
+    G = HQ // HKV
+    cl = torch.tensor([L1M], dtype=torch.int32, device=dev)
+    par = torch.tensor([-1, 0, 1], dtype=torch.int32, device=dev)
+    shards = []
+    for li, lay in enumerate(layers):
+        h = li % HKV
+        sl = slice(h * G, (h + 1) * G)
+        shards.append(dict(
+            k=lay["k"][:, h:h + 1], v=lay["v"][:, h:h + 1],
+            tree_k=lay["tree_k"][:, h:h + 1], tree_v=lay["tree_v"][:, h:h + 1],
+            verify_q=lay["verify_q"][:, :, sl].contiguous(), ctx_q=lay["ctx_q"][:, :, sl].contiguous(),
+            fwd_q=[f[:, :, sl].contiguous() for f in lay["fwd_q"]]))
+    dims = skg.make_dims(1, G, 1, D, skg.SPEC_BF16)
+    ws_v = skg.new_workspace(skg.verify_workspace_bytes(dims, CHAIN, L1M), dev)
+    ws_c = skg.new_workspace(skg.draft_workspace_bytes(dims, CHAIN, SINK + WINDOW + CHAIN - 1), dev)
+    ws_f = skg.new_workspace(skg.draft_workspace_bytes(dims, 1, SINK + WINDOW), dev)
+    v_out = torch.empty((1, CHAIN, G, D), dtype=torch.bfloat16, device=dev)
+    c_out = torch.empty_like(v_out)
+    f_out = torch.empty((1, 1, G, D), dtype=torch.bfloat16, device=dev)
+
+    def verify_pass():
+        for s in shards:
+            skg.spec_attn_verify_tree(s["verify_q"], s["k"], s["v"], cl, s["tree_k"], s["tree_v"],
+                                      par, out=v_out, want_lse=False, want_pos_ids=False,
+                                      workspace=ws_v)
+
+    def draft_pass():
+        for s in shards:
+            skg.spec_attn_draft_sparse(s["ctx_q"], s["k"], s["v"], cl, n_sink=SINK, window=WINDOW,
+                                       out=c_out, want_lse=False, workspace=ws_c)
+            for fq in s["fwd_q"]:
+                skg.spec_attn_draft_sparse(fq, s["k"], s["v"], cl, n_sink=SINK, window=WINDOW,
+                                           out=f_out, want_lse=False, workspace=ws_f)
+
+    res = {}
+    for name, fn in (("verify", verify_pass), ("drafts", draft_pass)):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        prerecord([a, b], torch)
+        torch.cuda._sleep(int(3e7))
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        res[name] = a.elapsed_time(b) / reps * 1e3 / len(shards)
+    for w in (ws_v, ws_c, ws_f):
+        assert skg.spec_device_status(w) == 0
+    vbytes = verify_bytes(1, L1M, CHAIN) // HKV
+    view = window_view_len(L1M, CHAIN, SINK, WINDOW)
+    return dict(kv_heads=1, q_heads=G, context=L1M,
+                verify_us_per_layer=round(res["verify"], 2),
+                verify_gbs=round(vbytes / (res["verify"] * 1e-6) / 1e9, 1),
+                drafts_us_per_layer=round(res["drafts"], 2),
+                attention_ms_per_step=round((res["verify"] + res["drafts"]) * len(shards) * 1e-3, 3),
+                note="one KV head per layer of the 32, as under 8-way KV-head sharding; "
+                     "drafts = one 3-query and three single-query calls")
+
+
 # ------------------------------------------------------------ budget selection
 
 def run_select(torch, skg, *, B=8, L=16384, block=16, reps=24, seed=8400):
@@ -1131,6 +1201,9 @@ def main():
     ring = run_ring_1m(torch, skg, layers)
     log(f"[bench] ring drafts: {ring['draft_us_per_layer_ring']} us per layer "
         f"(full cache {ring['draft_us_per_layer_full_cache']} us)")
+    shard = run_shard_1m(torch, skg, layers)
+    log(f"[bench] 8-way KV-head shard of the 1M step: verify {shard['verify_us_per_layer']} us "
+        f"per layer ({shard['verify_gbs']} GB/s), drafts {shard['drafts_us_per_layer']} us")
     partial = run_partial_1m(torch, skg, layers)
     partial["verify_full_us_per_layer"] = round(r1m["verify_avg_ms"] * 1e3, 2)
     log(f"[bench] partial verify: {partial['verify_partial_us_per_layer']} us per layer "
@@ -1224,6 +1297,7 @@ def main():
         "budget_select": select,
         "partial_verify_1m": partial,
         "ring_draft_1m": ring,
+        "shard_1m_kv1": shard,
     }
     print(json.dumps(line), flush=True)
 

@@ -158,9 +158,12 @@ Plan bf16_plan(const spec_dims* d, int32_t T, int64_t tiles, bool gather, bool v
   // Long register-staged splits take their tiles in chunks (dynamic
   // balancing across XCDs); budget gathers keep fixed ranges (their indices
   // are staged per range), and so does the deterministic mode (which wave
-  // sums which tiles would otherwise depend on timing).
+  // sums which tiles would otherwise depend on timing).  The pool's counter
+  // is one address per (pair, row block): with fewer than 8 of them, every
+  // wave's requests queue on a few addresses and the pool costs more than it
+  // balances (one KV head over 1M keys: 100.3 us pooled, 93.0 us fixed).
   if (p.wk == 4 && !gather && p.splits > 1 && tiles >= (int64_t)p.splits * 32 &&
-      !(d->flags & SPEC_FLAG_DETERMINISTIC))
+      groups >= kMinPoolGroups && !(d->flags & SPEC_FLAG_DETERMINISTIC))
     p.dyn = kChunkTiles;
   p.cnt_off = kHeaderBytes;
   size_t off = kScratchOff;

@@ -38,6 +38,7 @@ constexpr int kMaxGatherKeys = 2048;           // budget indices one workgroup s
 constexpr int kMaxPadWords = 1024;             // 32-key pad words one workgroup stages in LDS
 constexpr int kMergeFan = 16;                  // partials one split-merge step reads
 constexpr int kMaxSplits = kMergeFan * kMergeFan;
+constexpr int kMinPoolGroups = 8;             // (pair, row block) groups that make a chunk pool pay
 constexpr int kChunkTiles = 8;                 // tiles per dynamically taken chunk
 constexpr int kMaxOrderBatch = 256;            // tree verify: longest-first work order up to this batch
 constexpr int kOrderTiles = 384;               // tree verify (ordered): at most this many tiles per split

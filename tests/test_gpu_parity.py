@@ -162,6 +162,37 @@ def test_16k_accept(c16k):
     np.testing.assert_array_equal(got[0], a.expected_len)
 
 
+# ------------------------------------------------------------ more than 256 splits
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_verify_of_one_kv_head_over_half_a_million_keys(D):
+    """One (sequence, KV head) pair, a chain of 3 over 524,288 keys: the most
+    splits a call takes (256, two merge levels of 16), and fixed tile ranges
+    even without the deterministic flag (a single pair takes no chunk pool).
+    Every call against the oracle; all three calls bitwise equal."""
+    L = 1 << 19
+    case = synth.make_attn_case(7100 + D, B=1, Hq=4, Hkv=1, D=D, L_cap=L, T=3,
+                                value_scale=1 / math.sqrt(D))
+    tree = synth.chain_tree(3)
+    rng = case.extra["rng"]
+    tk = synth.draw_normal(rng, (1, 1, 3, D), 1 / math.sqrt(D), "bf16")
+    tv = synth.draw_normal(rng, (1, 1, 3, D), 1 / math.sqrt(D), "bf16")
+    ref, lse_ref = oracle.verify_attn_ref(case.q, case.k, case.v, case.cache_len, tk, tv,
+                                          tree.parents, scale=case.scale)
+    q, k, v, cl = dev(case.q), dev(case.k), dev(case.v), dev(case.cache_len)
+    par = dev(tree.parents.astype(np.int32))
+    outs = []
+    for det in (False, True, True):
+        out, lse, pos = skg.spec_attn_verify_tree(q, k, v, cl, dev(tk), dev(tv), par,
+                                                  scale=case.scale, deterministic=det)
+        torch.cuda.synchronize()
+        assert_close(host64(out), ref, "bf16", f"one head, 512K keys, D={D}"
+                     + (" (deterministic)" if det else ""))
+        assert_lse_close(lse.cpu().numpy().astype(np.float64), lse_ref, 1e-3, "512K lse")
+        outs.append(out.view(torch.int16).cpu().numpy())
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[1], outs[2])
+
+
 # ------------------------------------------------------------ peaked variants
 # The workloads draw N(0,1)/sqrt(128) values, so their scores spread by about
 # 0.01 and the attention is nearly uniform.  These variants draw queries,
