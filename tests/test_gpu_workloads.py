@@ -129,6 +129,31 @@ def test_1m_window_draft_sampled(layer1m, which):
         assert_lse_close(lse[:, :, g * G:(g + 1) * G], lse_ref, 1e-3, "1M draft lse")
 
 
+def test_1m_verify_every_layer_one_head():
+    """All 32 seeded layers of the 1M step (seeds 4000..4031), one after
+    another as the benchmark builds them: the chain-3 verify over 1,048,576
+    keys on one shared workspace, KV head (layer mod 8) of each checked
+    against the oracle, so every KV head is checked on four layers."""
+    cl = torch.tensor([L1M], dtype=torch.int32, device="cuda")
+    par = torch.tensor([-1, 0, 1], dtype=torch.int32, device="cuda")
+    dims = skg.make_dims(1, 32, 8, 128, skg.SPEC_BF16)
+    ws = skg.new_workspace(skg.verify_workspace_bytes(dims, 3, L1M), "cuda")
+    for layer in range(32):
+        d = dg.layer_1m(layer)
+        out, lse, _ = skg.spec_attn_verify_tree(d["verify_q"], d["k"], d["v"], cl, d["tree_k"],
+                                                d["tree_v"], par, workspace=ws)
+        torch.cuda.synchronize()
+        g = layer % 8
+        ref, lse_ref = verify_pair_ref(d, 0, g, L1M, np.array([-1, 0, 1]))
+        assert_close(host64(out)[:, :, g * G:(g + 1) * G], ref, "bf16",
+                     f"1M layer {layer} verify kv head {g}")
+        assert_lse_close(lse.cpu().numpy().astype(np.float64)[:, :, g * G:(g + 1) * G], lse_ref,
+                         1e-3, "1M verify lse")
+        del d, out, lse
+    assert skg.spec_device_status(ws) == 0
+    torch.cuda.empty_cache()
+
+
 def test_1m_peaked_layer_sampled():
     """A peaked 1M layer (every draw N(0, 1) unscaled, seed 4000 + 31): the
     chain-3 verify over 1,048,576 keys and the 3-query context draft, each on
