@@ -8,6 +8,7 @@
 
 #include <algorithm>
 #include <string>
+#include <vector>
 
 #include "spec_internal.h"
 
@@ -128,10 +129,10 @@ Plan bf16_plan(const spec_dims* d, int32_t T, int64_t tiles, bool gather, bool v
   // than the cross-workgroup merge a second split brings (a budget of 256 of
   // the 16K batch of 8: 10.2 -> 8.0 us per call, device time).
   if (p.wk == 4 && !verify && tiles <= 16) S = 1;
-  // A tree verify runs its splits longest sequence first, and the splits
-  // past a sequence's own length exit at once; so that a ragged batch's long
-  // sequences are spread over many workgroups, no split covers more than
-  // kOrderTiles tiles of the capacity.
+  // A tree verify sizes its splits on the device from the sequences' own
+  // lengths (see the kernel), at most S per sequence and none shorter than
+  // tiles / S; S covers the capacity in splits of at most kOrderTiles tiles,
+  // so that a ragged batch's long sequences spread over several workgroups.
   if (verify && p.wk == 1 && d->batch <= kMaxOrderBatch) {
     p.ordered = 1;
     S = std::max(S, cdiv(tiles, kOrderTiles));
@@ -155,6 +156,19 @@ Plan bf16_plan(const spec_dims* d, int32_t T, int64_t tiles, bool gather, bool v
   p.tps = (int32_t)cdiv(tiles, S);
   p.splits = (int32_t)cdiv(tiles, p.tps);
   p.n_blk = (int32_t)cdiv(p.splits, kMergeFan);
+  if (p.ordered) {
+    // The device takes T = clamp(total tiles / conc, tps, tps_max) tiles per
+    // split and gives sequence b ceil(tiles_b / T) splits (at most `splits`).
+    // While the batch's tiles cannot exceed conc * tps_max, T is never
+    // clamped from above, so the splits number at most conc + B: that many
+    // work items per (KV head, row block) cover every sequence.
+    p.conc = (int32_t)std::max<int64_t>(1, kTargetWorkgroups / ((int64_t)d->n_kv_heads * p.n_rb));
+    p.tps_max = kMaxPadWords;
+    const int64_t all = (int64_t)d->batch * p.splits;
+    p.items = (int32_t)((int64_t)d->batch * tiles <= (int64_t)p.conc * p.tps_max
+                            ? std::min<int64_t>(all, (int64_t)d->batch + p.conc)
+                            : all);
+  }
   // Long register-staged splits take their tiles in chunks (dynamic
   // balancing across XCDs); budget gathers keep fixed ranges (their indices
   // are staged per range), and so does the deterministic mode (which wave
@@ -267,7 +281,8 @@ int64_t draft_max_view(const spec_kv* cache, int32_t Tq, int32_t n_sink, int32_t
 
 // Workgroups (bf16) or wavefronts (fp32) of one attention launch.
 int64_t grid_size(const spec_dims* d, const Plan& p) {
-  const int64_t units = (int64_t)d->batch * d->n_kv_heads * p.splits;
+  const int64_t units = p.ordered ? (int64_t)p.items * d->n_kv_heads
+                                  : (int64_t)d->batch * d->n_kv_heads * p.splits;
   if (d->dtype != SPEC_BF16) return units * p.n_rb;
   return p.n_rb == 1 ? units : cdiv(units, 8) * 8 * p.n_rb;
 }
@@ -279,7 +294,7 @@ void fill_plan(AttnArgs& a, const Plan& p, void* workspace) {
   a.splits = p.splits;
   a.chunk = p.chunk;
   a.tps = p.tps;
-  a.units = a.B * a.Hkv * p.splits;
+  a.units = p.ordered ? p.items * a.Hkv : a.B * a.Hkv * p.splits;
   a.o_part = reinterpret_cast<float*>(ws + p.o_off);
   a.lse_part = reinterpret_cast<float*>(ws + p.lse_off);
   a.o_part1 = reinterpret_cast<float*>(ws + p.o1_off);
@@ -292,6 +307,9 @@ void fill_plan(AttnArgs& a, const Plan& p, void* workspace) {
   a.cnt_chunk = a.cnt_pos + 2 * (size_t)a.B;
   a.dyn = p.dyn;
   a.ordered = p.ordered;
+  a.items = p.items;
+  a.conc = p.conc;
+  a.tps_max = p.tps_max;
   a.err = reinterpret_cast<uint32_t*>(ws);
 }
 
@@ -991,6 +1009,35 @@ int32_t spec_debug_check_plan(const spec_dims* d, int32_t mode, int32_t T, int64
       const int64_t wend = std::min<int64_t>(t1, cache_tiles_max);
       if (wend - t0 > kMaxPadWords) return bad("split %d stages %lld pad words", s, (long long)(wend - t0));
     }
+  }
+  if (verify && p.ordered) {
+    // the kernel's balanced plan, for a few length patterns: every split
+    // must have a work item, stage at most tps_max pad words, and its
+    // partial slot must lie inside the split-partial buffer
+    if (p.tps_max > kMaxPadWords || p.tps > p.tps_max || p.conc < 1) return bad("ordered bounds");
+    if ((int64_t)p.items > (int64_t)d->batch * p.splits) return bad("ordered items");
+    const int64_t cap_tiles = cdiv(extent, kTileKeys), nt = cdiv(T, kTileKeys);
+    for (int pattern = 0; pattern < 4; ++pattern) {
+      int64_t W = 0, n_items = 0;
+      std::vector<int64_t> tl(d->batch);
+      for (int b = 0; b < d->batch; ++b) {
+        const int64_t len_tiles = pattern == 0 ? cap_tiles
+                                : pattern == 1 ? 0
+                                : pattern == 2 ? (b == 0 ? cap_tiles : 0)
+                                               : (cap_tiles * (b + 1)) / d->batch;
+        tl[b] = len_tiles + nt;
+        W += tl[b];
+      }
+      const int64_t tgt = std::min<int64_t>(p.tps_max, std::max<int64_t>(p.tps, cdiv(W, p.conc)));
+      for (int b = 0; b < d->batch; ++b) {
+        const int64_t sb = std::min<int64_t>(p.splits, cdiv(tl[b], tgt));
+        if (cdiv(tl[b], sb) > p.tps_max) return bad("ordered split of %lld tiles", (long long)cdiv(tl[b], sb));
+        n_items += sb;
+      }
+      if (n_items > p.items) return bad("%lld splits for %d items", (long long)n_items, p.items);
+    }
+    if ((uint64_t)d->n_kv_heads * p.n_rb * p.items > (uint64_t)groups * p.splits)
+      return bad("item slots overrun the split partials");
   }
   if (grid_size(d, p) > kMaxGrid) return bad("grid");
   return 0;

@@ -373,28 +373,63 @@ void attn_bf16_kernel(AttnArgs a) {
     if (unit >= a.units) return;
   }
   int s = unit % a.splits, pair = unit / a.splits;
+  // this workgroup's partial slot in its group's buffer, the first slot of
+  // its (sequence, KV head), and the split size of the sequence
+  int pslot = s, pslot0 = 0, tps_own = a.tps, S_ord = 0;
   if constexpr (MODE == kVerify && WK == 1) {
     if (a.ordered) {
-      // Splits in order of split index, and within one index the sequences
-      // longest first (ties: smaller index), so that the hardware starts the
-      // longest work first; a split past its sequence's length exits below.
-      __shared__ int32_t len_s[kMaxOrderBatch], ord_s[kMaxOrderBatch];
+      // Balanced splits, longest first.  Every workgroup reads all the
+      // sequences' lengths and derives the same plan: with W tiles in the
+      // batch (per KV head) and `conc` workgroups of a (KV head, row block)
+      // running at once, a split takes about T = W / conc tiles (clamped to
+      // [tps, tps_max]), sequence b gets ceil(tiles_b / T) equal splits, and
+      // the splits are numbered as work items in order of size, largest
+      // first (ties: smaller sequence index), so that the hardware starts the
+      // longest work first.  Workgroup j of a KV head takes item j; items past
+      // the last split exit.
+      // (the tile ring is free until the first copies: it holds the plan)
+      static_assert(Cf::RING >= 3 * kMaxOrderBatch * 4, "the ring holds the ordered plan");
+      int32_t* const tl_s = reinterpret_cast<int32_t*>(ring);   // tiles per sequence
+      int32_t* const ns_s = tl_s + kMaxOrderBatch;              // splits per sequence
+      int32_t* const st_s = ns_s + kMaxOrderBatch;              // first item of each sequence
+      __shared__ int32_t sel_s[1];
+      const int nt = (a.T + kTileKeys - 1) / kTileKeys;   // tree tiles
+      int w = 0;
       for (int i = threadIdx.x; i < a.B; i += 256) {
         const int l = a.cache_len[i];
-        len_s[i] = (l >= 0 && l <= a.capacity) ? l : 0;
+        const int tl = ((l >= 0 && l <= a.capacity) ? (l + kTileKeys - 1) / kTileKeys : 0) + nt;
+        tl_s[i] = tl;
+        w += tl;
       }
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) w += __shfl_xor(w, m, 64);
+      if ((threadIdx.x & 63) == 0) red_s[threadIdx.x >> 6] = w;
+      if (threadIdx.x == 0) sel_s[0] = -1;
       __syncthreads();
+      const int W = red_s[0] + red_s[1] + red_s[2] + red_s[3];
+      const int tgt = min(a.tps_max, max(a.tps, (W + a.conc - 1) / a.conc));
+      for (int i = threadIdx.x; i < a.B; i += 256) ns_s[i] = min(a.splits, (tl_s[i] + tgt - 1) / tgt);
+      __syncthreads();
+      const int item = unit / a.Hkv;
       for (int i = threadIdx.x; i < a.B; i += 256) {
-        const int li = len_s[i];
-        int r = 0;
-        for (int j = 0; j < a.B; ++j) r += (len_s[j] > li) || (len_s[j] == li && j < i);
-        ord_s[r] = i;
+        const int si = (tl_s[i] + ns_s[i] - 1) / ns_s[i];
+        int start = 0;
+        for (int j = 0; j < a.B; ++j) {
+          const int sj = (tl_s[j] + ns_s[j] - 1) / ns_s[j];
+          start += (sj > si || (sj == si && j < i)) ? ns_s[j] : 0;
+        }
+        st_s[i] = start;
+        if (item >= start && item < start + ns_s[i]) sel_s[0] = i;   // one sequence matches
       }
       __syncthreads();
-      const int pairs = a.B * a.Hkv;
-      s = unit / pairs;
-      const int k = unit % pairs;
-      pair = ord_s[k / a.Hkv] * a.Hkv + k % a.Hkv;
+      const int bb = sel_s[0];
+      if (bb < 0) return;   // past the batch's last split: nothing to do
+      pslot0 = st_s[bb];
+      s = item - pslot0;
+      pslot = item;
+      S_ord = ns_s[bb];
+      tps_own = (tl_s[bb] + S_ord - 1) / S_ord;
+      pair = bb * a.Hkv + unit % a.Hkv;
     }
   }
   const int b = pair / a.Hkv, g = pair % a.Hkv;
@@ -412,17 +447,12 @@ void attn_bf16_kernel(AttnArgs a) {
   bool bad = MODE == kVerify ? (L < 0 || L > a.capacity)
                              : (L < T || (a.kv_ring == 0 && L > a.capacity));   // a ring keeps the logical length
   if (leader && tid == 0 && bad) raise_error(a.err, SPEC_DEV_CACHE_LEN);
-  // Splits of this (sequence, KV head) that hold work: all of them, or, in
-  // the ordered verify, those that start below the sequence's own key count
-  // (a sequence with a bad length keeps one, which writes its poisoned rows).
+  // Splits of this (sequence, KV head): all of the plan's, or, in the
+  // ordered verify, the sequence's own (a sequence with a bad length has
+  // one, which writes its poisoned rows).
   int S_own = a.splits;
   if constexpr (MODE == kVerify && WK == 1) {
-    if (a.ordered) {
-      const int Lv = bad ? 0 : L;
-      const int keys_tiles = (Lv + kTileKeys - 1) / kTileKeys + (N + kTileKeys - 1) / kTileKeys;
-      S_own = max(1, min(a.splits, (keys_tiles + a.tps - 1) / a.tps));
-      if (s >= S_own) return;
-    }
+    if (a.ordered) S_own = S_ord;
   }
 
   // ---------------------------------------------------------------- tree
@@ -467,7 +497,7 @@ void attn_bf16_kernel(AttnArgs a) {
   const int tree_tiles = (MODE == kVerify && !bad) ? (N + kTileKeys - 1) / kTileKeys : 0;
   const int total = cache_tiles + tree_tiles;
   int t0, t1;
-  split_tiles(total, a.tps, s, t0, t1);
+  split_tiles(total, tps_own, s, t0, t1);
   int k0 = t0, k1 = t1;
   if constexpr (WK == 4) {
     const int per = (t1 - t0 + 3) / 4;
@@ -938,12 +968,16 @@ void attn_bf16_kernel(AttnArgs a) {
     lr[rt] += shfl_xor(lr[rt], 16);
     lr[rt] += shfl_xor(lr[rt], 32);
   }
-  const int S = a.splits;   // the partial buffers' split dimension
   const int So = S_own;      // splits of this pair that write a partial
-  const size_t grp = (size_t)pair * a.n_rb + z;
-  // this group's partials: o [S][RC][D], lse [S][RC] (log2 domain)
-  const __amdgpu_buffer_rsrc_t o_rs = coherent_rsrc(a.o_part + grp * S * RC * D, (uint32_t)(S * RC * D * 4));
-  const __amdgpu_buffer_rsrc_t l_rs = coherent_rsrc(a.lse_part + grp * S * RC, (uint32_t)(S * RC * 4));
+  const size_t grp = (size_t)pair * a.n_rb + z;   // counters and block partials
+  // split partials: o [S][RC][D], lse [S][RC] (log2 domain) per (pair, row
+  // block), or, in the ordered verify, per (KV head, row block) with one
+  // slot per work item
+  const bool per_item = MODE == kVerify && WK == 1 && a.ordered;
+  const int S = per_item ? a.items : a.splits;
+  const size_t pgrp = per_item ? (size_t)g * a.n_rb + z : grp;
+  const __amdgpu_buffer_rsrc_t o_rs = coherent_rsrc(a.o_part + pgrp * S * RC * D, (uint32_t)(S * RC * D * 4));
+  const __amdgpu_buffer_rsrc_t l_rs = coherent_rsrc(a.lse_part + pgrp * S * RC, (uint32_t)(S * RC * 4));
   const int R = a.R, Hq = a.Hq;
   uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
   float* lse_out = a.lse;
@@ -954,8 +988,8 @@ void attn_bf16_kernel(AttnArgs a) {
     const int row = z * RC + row_l;
     if (row >= R) return;
     if (So > 1) {
-      store_sc1_f4(o_rs, (uint32_t)(((s * RC + row_l) * D + d0) * 4), f32x4{vals[0], vals[1], vals[2], vals[3]});
-      if (lse_lane) store_sc1_f1(l_rs, (uint32_t)((s * RC + row_l) * 4), lse2);
+      store_sc1_f4(o_rs, (uint32_t)(((pslot * RC + row_l) * D + d0) * 4), f32x4{vals[0], vals[1], vals[2], vals[3]});
+      if (lse_lane) store_sc1_f1(l_rs, (uint32_t)((pslot * RC + row_l) * 4), lse2);
       return;
     }
     const int t = row / G, hh = row % G;
@@ -1063,12 +1097,12 @@ void attn_bf16_kernel(AttnArgs a) {
   };
   if (nb == 1) {
     reset_chunks();
-    merge_partials<D, RC>(o_rs, l_rs, 0, So, rows, final_sink);
+    merge_partials<D, RC>(o_rs, l_rs, pslot0, So, rows, final_sink);
     return;
   }
   const __amdgpu_buffer_rsrc_t o1_rs = coherent_rsrc(a.o_part1 + grp * a.n_blk * RC * D, (uint32_t)(a.n_blk * RC * D * 4));
   const __amdgpu_buffer_rsrc_t l1_rs = coherent_rsrc(a.lse_part1 + grp * a.n_blk * RC, (uint32_t)(a.n_blk * RC * 4));
-  merge_partials<D, RC>(o_rs, l_rs, blk * kMergeFan, bsz, rows,
+  merge_partials<D, RC>(o_rs, l_rs, pslot0 + blk * kMergeFan, bsz, rows,
                         [&](int rl, int d0, const float* o, float lse2) __attribute__((always_inline)) {
                           store_sc1_f4(o1_rs, (uint32_t)(((blk * RC + rl) * D + d0) * 4), f32x4{o[0], o[1], o[2], o[3]});
                           if (d0 == 0) store_sc1_f1(l1_rs, (uint32_t)((blk * RC + rl) * 4), lse2);

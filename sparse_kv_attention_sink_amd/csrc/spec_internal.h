@@ -41,7 +41,7 @@ constexpr int kMaxSplits = kMergeFan * kMergeFan;
 constexpr int kMinPoolGroups = 8;             // (pair, row block) groups that make a chunk pool pay
 constexpr int kChunkTiles = 8;                 // tiles per dynamically taken chunk
 constexpr int kMaxOrderBatch = 256;            // tree verify: longest-first work order up to this batch
-constexpr int kOrderTiles = 384;               // tree verify (ordered): at most this many tiles per split
+constexpr int kOrderTiles = 384;               // tree verify (ordered): capacity tiles per planned split, at most
 constexpr int kCompactSlices = 64;             // pad-scan workgroups per sequence (compaction)
 constexpr int kCompactScanSlots = 65536;       // compaction: longer pad rows are scanned in slices
 constexpr int kMaxSelectBlocks = 8192;         // candidate blocks one selection scores
@@ -95,7 +95,10 @@ struct AttnArgs {
   uint32_t* cnt_pos;      // [B][2] pad-count arrival (verify positions)
   uint32_t* cnt_chunk;    // bf16 path: [pair][n_rb] next tile chunk (dynamic splits)
   int32_t dyn;            // bf16 path: tiles per dynamically taken chunk, 0 = fixed ranges
-  int32_t ordered;        // bf16 tree verify: splits in longest-sequence-first order, empty ones exit
+  int32_t ordered;        // bf16 tree verify: balanced splits, longest first (see the kernel)
+  int32_t items;          // ordered: work items per (KV head, row block); partial slots per group
+  int32_t conc;           // ordered: workgroups per (KV head, row block) that run at once
+  int32_t tps_max;        // ordered: the most tiles one split may take (its staged pad words)
   void* out;              // final output
   float* lse;             // final lse (natural log) or null
   uint32_t* err;          // device error word
@@ -109,6 +112,7 @@ struct Plan {
   int32_t n_blk = 1;
   int32_t dyn = 0;          // tiles per dynamically taken chunk (0: fixed split ranges)
   int32_t ordered = 0;      // tree verify in longest-first order (see AttnArgs)
+  int32_t items = 0, conc = 0, tps_max = 0;   // ordered only
 };
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
