@@ -85,8 +85,8 @@ struct AttnArgs {
   int32_t tps;            // bf16 path: tiles per split
   int32_t units;          // bf16 path: pairs * splits
   // outputs
-  float* o_part;          // [pair][n_rb][splits][rb][D]
-  float* lse_part;        // [pair][n_rb][splits][rb]   (log2 domain)
+  float* o_part;          // [pair][n_rb][splits][rb][D]; ordered: [Hkv][n_rb][items][rb][D]
+  float* lse_part;        // [pair][n_rb][splits][rb]   (log2 domain; ordered: by item)
   float* o_part1;         // bf16 path: [pair][n_rb][n_blk][rb][D] block merges
   float* lse_part1;       // bf16 path: [pair][n_rb][n_blk][rb]
   int32_t n_blk;          // bf16 path: ceil(splits / kMergeFan)
