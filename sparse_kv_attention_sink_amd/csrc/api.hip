@@ -102,8 +102,15 @@ Plan bf16_plan(const spec_dims* d, int32_t T, int64_t tiles, bool gather, bool v
     p.rt = (pairs <= 16) ? 1 : (int32_t)cdiv(p.rows, 16);
     p.rb = 16 * p.rt;
   } else {                      // many rows: one shared ring, 4 x 16*rt rows
+    // Up to 128 rows take one or two 16-row tiles per wavefront; 129 to 192
+    // rows (a 44-node tree with 4 query heads per KV head: 176) take three,
+    // so that each tile is read once instead of by two row blocks (the
+    // 16K batch of 8: 164 -> 154 us; the ragged batch: 319 -> 302 us).
+    // More rows take row blocks of 128: a 256-row block would need 64 rows
+    // per wavefront, more registers than two wavefronts per SIMD allow.
     p.wk = 1;
-    p.rt = (int32_t)std::min<int64_t>(2, cdiv(p.rows, 64));
+    const int64_t r64 = cdiv(p.rows, 64);
+    p.rt = (int32_t)(r64 == 3 ? 3 : std::min<int64_t>(2, r64));
     p.rb = 64 * p.rt;
   }
   p.n_rb = (int32_t)cdiv(p.rows, p.rb);
@@ -168,6 +175,14 @@ Plan bf16_plan(const spec_dims* d, int32_t T, int64_t tiles, bool gather, bool v
     p.items = (int32_t)((int64_t)d->batch * tiles <= (int64_t)p.conc * p.tps_max
                             ? std::min<int64_t>(all, (int64_t)d->batch + p.conc)
                             : all);
+    // The kernel addresses a (KV head, row block)'s item partials with
+    // 32-bit signed byte offsets.  A batch whose items overflow them (only
+    // at hundreds of millions of cached keys) keeps the plain split order,
+    // whose partials are per (sequence, KV head, row block).
+    if ((int64_t)p.items * p.rb * d->head_dim * 4 > INT32_MAX) {
+      p.ordered = 0;
+      p.items = p.conc = p.tps_max = 0;
+    }
   }
   // Long register-staged splits take their tiles in chunks (dynamic
   // balancing across XCDs); budget gathers keep fixed ranges (their indices
@@ -1016,6 +1031,8 @@ int32_t spec_debug_check_plan(const spec_dims* d, int32_t mode, int32_t T, int64
     // partial slot must lie inside the split-partial buffer
     if (p.tps_max > kMaxPadWords || p.tps > p.tps_max || p.conc < 1) return bad("ordered bounds");
     if ((int64_t)p.items > (int64_t)d->batch * p.splits) return bad("ordered items");
+    if ((int64_t)p.items * p.rb * d->head_dim * 4 > INT32_MAX)
+      return bad("%d item partials exceed 32-bit offsets", p.items);
     const int64_t cap_tiles = cdiv(extent, kTileKeys), nt = cdiv(T, kTileKeys);
     for (int pattern = 0; pattern < 4; ++pattern) {
       int64_t W = 0, n_items = 0;

@@ -28,7 +28,8 @@
 //
 // Two shapes:
 //  * many rows (trees: nodes x GQA group > 32): the 4 wavefronts share one
-//    ring and each owns up to 64 rows (WK = 1);
+//    ring and each owns 16, 32 or 48 rows (one to three 16-row MFMA tiles,
+//    WK = 1);
 //  * few rows (chains, drafts): each wavefront streams its own quarter of the
 //    workgroup's tiles through a private ring and the four results are merged
 //    in LDS at the end (WK = 4).
@@ -339,7 +340,7 @@ struct AttnCfg {
 };
 
 template <int MODE, int D, int RT, int WK, int NS>
-__global__ __launch_bounds__(256, ((WK == 4 ? RT == 1 : RT <= 2) && 2 * AttnCfg<MODE, D, RT, WK, NS>::RING <= 136 * 1024) ? 2 : 1)
+__global__ __launch_bounds__(256, ((WK == 4 ? RT == 1 : RT <= 3) && 2 * AttnCfg<MODE, D, RT, WK, NS>::RING <= 136 * 1024) ? 2 : 1)
 void attn_bf16_kernel(AttnArgs a) {
   using Cf = AttnCfg<MODE, D, RT, WK, NS>;
   using Ge = Geo<D>;
@@ -508,21 +509,20 @@ void attn_bf16_kernel(AttnArgs a) {
   // ---------------------------------------------------------------- rows
   // (the query loads are issued first, so that their latency overlaps the
   // staging loads below and the first tile's loads)
+  // erow: a draft row's end position; in verify, the row's tree node (-1
+  // past the last row), whose ancestor mask tree tiles read from LDS
   bf16x8 qf[RT][ND];
   int erow[RT];
-  uint64_t ancr[RT];
   const int row0 = z * RC + rg * RCW;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int row = row0 + rt * 16 + l16;
-    erow[rt] = 0;
-    ancr[rt] = 0;
+    erow[rt] = MODE == kVerify ? -1 : 0;
 #pragma unroll
     for (int c = 0; c < ND; ++c) qf[rt][c] = bf16x8{};
     if (row < a.R) {
       const int t = row / G, hh = row % G;
-      erow[rt] = L - T + t + 1;
-      if constexpr (MODE == kVerify) ancr[rt] = anc_s[t];
+      erow[rt] = MODE == kVerify ? t : L - T + t + 1;
       const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
                            (((size_t)b * T + t) * a.Hq + g * G + hh) * D + q4 * 8;
 #pragma unroll
@@ -771,30 +771,56 @@ void attn_bf16_kernel(AttnArgs a) {
     const bool full = !tree_tile && (t + 1) * kTileKeys <= n_view && !row_masks && pw == 0u;
 
     // K fragments (A operand of S^T): key h*16 + l16, head-dim chunk cc*4 + q4;
-    // V^T fragments (A operand of O^T) for every d tile, read now so that
-    // their latency hides behind the scores and the softmax.
-    bf16x8 kf[2][ND], vf[NDT];
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int cc = 0; cc < ND; ++cc) kf[h][cc] = lds_load_b128(koff[cc] + so + h * 16 * ROWB);
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
+    // V^T fragments (A operand of O^T) of d tile dt.
+    auto read_v = [&](int dt) __attribute__((always_inline)) {
       const s16x4 v0 = lds_read_tr16(voff[dt] + so);
       const s16x4 v1 = lds_read_tr16(voff[dt] + so + 16 * ROWB);
-      vf[dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-    }
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    // With up to two row tiles every fragment of the tile is read at once
+    // (the V^T fragments' latency then hides behind the scores and the
+    // softmax).  Three row tiles need those registers: K is read one 16-key
+    // half at a time and V^T one half of the d tiles at a time, each read
+    // issued behind independent MFMAs of the same wavefront.
+    constexpr int NV = RT >= 3 ? NDT / 2 : NDT;   // V^T fragments held at once
+    bf16x8 vf[NV];
     f32x4 sc[RT][2];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+    if constexpr (RT >= 3) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
+        bf16x8 kh[ND];
 #pragma unroll
-        for (int cc = 0; cc < ND; ++cc)
-          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[h][cc], qf[rt][cc], c, 0, 0, 0);
-        sc[rt][h] = c;
+        for (int cc = 0; cc < ND; ++cc) kh[cc] = lds_load_b128(koff[cc] + so + h * 16 * ROWB);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int cc = 0; cc < ND; ++cc)
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh[cc], qf[rt][cc], c, 0, 0, 0);
+          sc[rt][h] = c;
+        }
       }
+#pragma unroll
+      for (int dt = 0; dt < NV; ++dt) vf[dt] = read_v(dt);
+    } else {
+      bf16x8 kf[2][ND];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int cc = 0; cc < ND; ++cc) kf[h][cc] = lds_load_b128(koff[cc] + so + h * 16 * ROWB);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) vf[dt] = read_v(dt);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int cc = 0; cc < ND; ++cc)
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[h][cc], qf[rt][cc], c, 0, 0, 0);
+          sc[rt][h] = c;
+        }
+    }
 
     // Visibility of this lane's 8 keys, local index e = h*4 + i, tile key
     // h*16 + q4*4 + i.  `full` tiles (every key visible to every row) skip it.
@@ -824,7 +850,8 @@ void attn_bf16_kernel(AttnArgs a) {
       if (!full) {
         uint32_t rm = kmask;
         if (tree_tile) {
-          const uint32_t aw = (uint32_t)(ancr[rt] >> ((t - cache_tiles) * kTileKeys));
+          const uint64_t an = erow[rt] >= 0 ? anc_s[erow[rt]] : 0ull;
+          const uint32_t aw = (uint32_t)(an >> ((t - cache_tiles) * kTileKeys));
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int kk = (e >> 2) * 16 + q4 * 4 + (e & 3);
@@ -893,14 +920,20 @@ void attn_bf16_kernel(AttnArgs a) {
       for (int w = 0; w < 4; ++w) pf[rt][w] = pack_bf16x2(p[rt][2 * w], p[rt][2 * w + 1]);
     }
 
-    // O^T += V^T . P^T
+    // O^T += V^T . P^T (three row tiles: the second half of the V^T
+    // fragments is read behind the first half's MFMAs)
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
+    for (int dt = 0; dt < NDT; ++dt) {
+      if (NV < NDT && dt == NV) {
+#pragma unroll
+        for (int d2 = 0; d2 < NV; ++d2) vf[d2] = read_v(NV + d2);
+      }
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(pf[rt][0], pf[rt][1], pf[rt][2], pf[rt][3]));
-        acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pb, acc[rt][dt], 0, 0, 0);
+        acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt % NV], pb, acc[rt][dt], 0, 0, 0);
       }
+    }
   };
 
   if constexpr (WK == 1) {
@@ -1130,7 +1163,8 @@ static hipError_t launch_mode(const AttnArgs& a, const Plan& p, hipStream_t st) 
     return launch_shape<MODE, D, 2, 4>(a, st);
   }
   if (p.rt == 1) return launch_shape<MODE, D, 1, 1>(a, st);
-  return launch_shape<MODE, D, 2, 1>(a, st);   // (the plan uses at most two 16-row tiles)
+  if (p.rt == 3) return launch_shape<MODE, D, 3, 1>(a, st);
+  return launch_shape<MODE, D, 2, 1>(a, st);
 }
 
 hipError_t launch_attn_bf16(const AttnArgs& a, int mode, const Plan& p, hipStream_t st) {

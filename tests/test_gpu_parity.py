@@ -356,6 +356,69 @@ def test_ragged_verify(shape, widths):
     np.testing.assert_array_equal(pos, oracle.position_ids(case.cache_len, pad, tree.parents))
 
 
+# ------------------------------------------------------------ three row tiles per wavefront
+# 129 to 192 query rows per (sequence, KV head) take one row block of four
+# wavefronts with three 16-row MFMA tiles each (48 rows), whose K and V
+# fragments are read in halves; rows past the last one compute on zero
+# queries and are never stored.
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("T,sink,win", [(40, 4, 300), (33, 0, 2000)])
+def test_window_draft_of_129_to_192_rows(D, T, sink, win):
+    B, Hq, Hkv, cap = 2, 8, 2, 2600
+    case = synth.make_attn_case(8800 + T + D, B=B, Hq=Hq, Hkv=Hkv, D=D, L_cap=cap, T=T,
+                                cache_len=[cap, 1000], dtype="bf16", value_scale=1.0)
+    got, lse = run_draft(case, n_sink=sink, window=win)
+    ref, lse_ref = oracle.draft_attn_ref(case.q, case.k, case.v, case.cache_len, scale=case.scale,
+                                         n_sink=sink, window=win)
+    assert_close(got, ref, "bf16", f"window draft, {T * Hq // Hkv} rows, D={D}")
+    assert_lse_close(lse, lse_ref, 1e-3, "window draft lse")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_budget_draft_of_129_to_192_rows(D):
+    B, Hq, Hkv, T, cap, budget = 2, 8, 2, 44, 3000, 700
+    rng = np.random.default_rng(8900 + D)
+    lens = [3000, 1500]
+    case = synth.make_attn_case(8901 + D, B=B, Hq=Hq, Hkv=Hkv, D=D, L_cap=cap, T=T,
+                                cache_len=lens, dtype="bf16", value_scale=1.0)
+    idx = np.stack([rng.integers(0, lens[b] - T, size=(Hkv, budget)) for b in range(B)]).astype(np.int32)
+    idx[:, :, ::9] = -1
+    got, lse = run_draft(case, idx=idx)
+    ref, lse_ref = oracle.draft_attn_ref(case.q, case.k, case.v, case.cache_len, scale=case.scale,
+                                         idx=idx)
+    assert_close(got, ref, "bf16", f"budget draft, {T * Hq // Hkv} rows, D={D}")
+    assert_lse_close(lse, lse_ref, 1e-3, "budget draft lse")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("Hq,Hkv,widths", [
+    (8, 2, (10, 14, 12, 8)),   # 44 nodes x GQA 4 = 176 rows
+    (16, 2, (4, 6, 6, 4)),     # 20 nodes x GQA 8 = 160 rows
+    (8, 2, (1,) * 48),         # a chain of 48 x GQA 4 = 192 rows, every slot used
+    (8, 2, (1,) * 33),         # 33 x GQA 4 = 132 rows: one row tile of the last wavefront used
+])
+def test_verify_of_129_to_192_rows(D, Hq, Hkv, widths):
+    B, cap = 3, 5000
+    lens = [5000, 37, 2100]
+    rng = np.random.default_rng(9000 + sum(widths) + D)
+    tree = synth.layered_tree(rng, widths)
+    N = tree.n
+    case = synth.make_attn_case(9001 + N + D, B=B, Hq=Hq, Hkv=Hkv, D=D, L_cap=cap, T=N,
+                                cache_len=lens, dtype="bf16", value_scale=1.0)
+    tk = synth.draw_normal(rng, (B, Hkv, N, D), 1.0, "bf16")
+    tv = synth.draw_normal(rng, (B, Hkv, N, D), 1.0, "bf16")
+    pad = np.zeros((B, cap), dtype=np.uint8)
+    for b in range(B):
+        pad[b, :lens[b]] = synth.pad_groups(rng, lens[b], n_groups=4, group=3)
+    got, lse, pos = run_verify(case, case.q, tk, tv, tree.parents, pad=pad)
+    ref, lse_ref = oracle.verify_attn_ref(case.q, case.k, case.v, case.cache_len, tk, tv,
+                                          tree.parents, scale=case.scale, pad=pad)
+    assert_close(got, ref, "bf16", f"verify, {N * Hq // Hkv} rows, D={D}")
+    assert_lse_close(lse, lse_ref, 1e-3, "verify lse")
+    np.testing.assert_array_equal(pos, oracle.position_ids(case.cache_len, pad, tree.parents))
+
+
 # ------------------------------------------------------------ tree-verify work order
 
 def test_verify_longest_first_with_empty_splits_and_two_merge_levels():
