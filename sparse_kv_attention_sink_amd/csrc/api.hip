@@ -102,15 +102,23 @@ Plan bf16_plan(const spec_dims* d, int32_t T, int64_t tiles, bool gather, bool v
     p.rt = (pairs <= 16) ? 1 : (int32_t)cdiv(p.rows, 16);
     p.rb = 16 * p.rt;
   } else {                      // many rows: one shared ring, 4 x 16*rt rows
-    // Up to 128 rows take one or two 16-row tiles per wavefront; 129 to 192
-    // rows (a 44-node tree with 4 query heads per KV head: 176) take three,
-    // so that each tile is read once instead of by two row blocks (the
-    // 16K batch of 8: 164 -> 154 us; the ragged batch: 319 -> 302 us).
-    // More rows take row blocks of 128: a 256-row block would need 64 rows
-    // per wavefront, more registers than two wavefronts per SIMD allow.
+    // Up to 128 rows take one or two 16-row tiles per wavefront, more rows
+    // row blocks of 128 or 192 (two or three tiles per wavefront; four would
+    // need more registers than two wavefronts per SIMD allow).  Every row
+    // block reads every tile, and three tiles per wavefront cost about a
+    // third more per (row, key) than two, so blocks of 192 are taken where
+    // they save a block and were measured to pay: 129 to 192 rows (a
+    // 44-node tree with 4 query heads per KV head: 176; the 16K batch of 8:
+    // 159.4 -> 148.8 us, the ragged batch of 16: 321.7 -> 295.0 us) and 257
+    // to 384 rows (44 nodes with 8 query heads per KV head: 352; the 16K
+    // batch of 8: 292.8 -> 227.4 us).  512 rows keep four blocks of 128
+    // (three of 192: 284.8 -> 390.3 us).
     p.wk = 1;
-    const int64_t r64 = cdiv(p.rows, 64);
-    p.rt = (int32_t)(r64 == 3 ? 3 : std::min<int64_t>(2, r64));
+    if (p.rows <= 128) {
+      p.rt = (int32_t)cdiv(p.rows, 64);
+    } else {
+      p.rt = (p.rows <= 192 || (p.rows > 256 && p.rows <= 384)) ? 3 : 2;
+    }
     p.rb = 64 * p.rt;
   }
   p.n_rb = (int32_t)cdiv(p.rows, p.rb);

@@ -419,6 +419,37 @@ def test_verify_of_129_to_192_rows(D, Hq, Hkv, widths):
     np.testing.assert_array_equal(pos, oracle.position_ids(case.cache_len, pad, tree.parents))
 
 
+# ------------------------------------------------------------ two row blocks of 128
+# 193 to 256 query rows per (sequence, KV head) take two row blocks of 128
+# rows (two 16-row tiles per wavefront), the second partly empty.
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("Hq,Hkv,widths", [
+    (8, 2, (10, 18, 18, 18)),   # 64 nodes x GQA 4 = 256 rows
+    (16, 2, (4, 8, 8, 8)),      # 28 nodes x GQA 8 = 224 rows
+    (8, 2, (1,) * 49),          # a chain of 49 x GQA 4 = 196 rows
+])
+def test_verify_of_193_to_256_rows(D, Hq, Hkv, widths):
+    B, cap = 3, 9000
+    lens = [9000, 45, 4100]
+    rng = np.random.default_rng(9100 + sum(widths) + D)
+    tree = synth.layered_tree(rng, widths)
+    N = tree.n
+    case = synth.make_attn_case(9101 + N + D, B=B, Hq=Hq, Hkv=Hkv, D=D, L_cap=cap, T=N,
+                                cache_len=lens, dtype="bf16", value_scale=1.0)
+    tk = synth.draw_normal(rng, (B, Hkv, N, D), 1.0, "bf16")
+    tv = synth.draw_normal(rng, (B, Hkv, N, D), 1.0, "bf16")
+    pad = np.zeros((B, cap), dtype=np.uint8)
+    for b in range(B):
+        pad[b, :lens[b]] = synth.pad_groups(rng, lens[b], n_groups=4, group=3)
+    got, lse, pos = run_verify(case, case.q, tk, tv, tree.parents, pad=pad)
+    ref, lse_ref = oracle.verify_attn_ref(case.q, case.k, case.v, case.cache_len, tk, tv,
+                                          tree.parents, scale=case.scale, pad=pad)
+    assert_close(got, ref, "bf16", f"verify, {N * Hq // Hkv} rows, D={D}")
+    assert_lse_close(lse, lse_ref, 1e-3, "verify lse")
+    np.testing.assert_array_equal(pos, oracle.position_ids(case.cache_len, pad, tree.parents))
+
+
 # ------------------------------------------------------------ tree-verify work order
 
 def test_verify_longest_first_with_empty_splits_and_two_merge_levels():
