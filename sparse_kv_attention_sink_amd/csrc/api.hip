@@ -145,12 +145,13 @@ Plan bf16_plan(const spec_dims* d, int32_t T, int64_t tiles, bool gather, bool v
   // the 16K batch of 8: 10.2 -> 8.0 us per call, device time).
   if (p.wk == 4 && !verify && tiles <= 16) S = 1;
   // A tree verify sizes its splits on the device from the sequences' own
-  // lengths (see the kernel), at most S per sequence and none shorter than
-  // tiles / S; S covers the capacity in splits of at most kOrderTiles tiles,
-  // so that a ragged batch's long sequences spread over several workgroups.
+  // lengths (see the kernel), at most S per sequence: S allows splits of
+  // kOrderTiles tiles over the capacity (up to one merge level of 16), so
+  // that a ragged batch's long sequences spread over as many workgroups as
+  // balance needs, and at most 384 tiles per split beyond.
   if (verify && p.wk == 1 && d->batch <= kMaxOrderBatch) {
     p.ordered = 1;
-    S = std::max(S, cdiv(tiles, kOrderTiles));
+    S = std::max({S, std::min<int64_t>(kMergeFan, cdiv(tiles, kOrderTiles)), cdiv(tiles, 384)});
   }
   S = std::min<int64_t>(std::max(S, lo), kMaxSplits);
   if (S < lo) {
@@ -205,7 +206,10 @@ Plan bf16_plan(const spec_dims* d, int32_t T, int64_t tiles, bool gather, bool v
   p.cnt_off = kHeaderBytes;
   size_t off = kScratchOff;
   if (p.splits > 1) {
-    const size_t n = (size_t)groups * p.splits * p.rb;
+    // split partials: one slot per (pair, row block, split), or, in the
+    // ordered verify, per (KV head, row block, work item)
+    const size_t n = p.ordered ? (size_t)d->n_kv_heads * p.n_rb * p.items * p.rb
+                               : (size_t)groups * p.splits * p.rb;
     p.o_off = off;
     off = align_up(off + n * d->head_dim * sizeof(float), 256);
     p.lse_off = off;
@@ -1009,10 +1013,14 @@ int32_t spec_debug_check_plan(const spec_dims* d, int32_t mode, int32_t T, int64
   if (p.cnt_off != kHeaderBytes || words > (int64_t)kCounterWords)
     return bad("%lld counter words exceed the region", (long long)words);
   if (p.splits > 1) {
-    const uint64_t part = (uint64_t)p.splits * p.rb * d->head_dim * 4;   // one group's o partials
+    // one group's slots: a (pair, row block)'s splits, or in the ordered
+    // verify a (KV head, row block)'s work items
+    const uint64_t slots = p.ordered ? (uint64_t)p.items : (uint64_t)p.splits;
+    const uint64_t n_groups = p.ordered ? (uint64_t)d->n_kv_heads * p.n_rb : (uint64_t)groups;
+    const uint64_t part = slots * p.rb * d->head_dim * 4;   // one group's o partials
     if (part > UINT32_MAX) return bad("a group's partials exceed a buffer descriptor");
-    if (p.o_off < kScratchOff || p.o_off + groups * part > p.lse_off ||
-        p.lse_off + (uint64_t)groups * p.splits * p.rb * 4 > (p.n_blk > 1 ? p.o1_off : p.total))
+    if (p.o_off < kScratchOff || p.o_off + n_groups * part > p.lse_off ||
+        p.lse_off + n_groups * slots * p.rb * 4 > (p.n_blk > 1 ? p.o1_off : p.total))
       return bad("split partials overlap");
   }
   if (p.n_blk > 1 && p.lse1_off + (uint64_t)groups * p.n_blk * p.rb * 4 > p.total)
@@ -1053,7 +1061,23 @@ int32_t spec_debug_check_plan(const spec_dims* d, int32_t mode, int32_t T, int64
         tl[b] = len_tiles + nt;
         W += tl[b];
       }
-      const int64_t tgt = std::min<int64_t>(p.tps_max, std::max<int64_t>(p.tps, cdiv(W, p.conc)));
+      // the kernel's search: the smallest T in [lo, hi] whose splits number
+      // at most conc
+      const auto count = [&](int64_t T) {
+        int64_t c = 0;
+        for (int b = 0; b < d->batch; ++b) c += std::min<int64_t>(p.splits, cdiv(tl[b], T));
+        return c;
+      };
+      int64_t lo = std::max<int64_t>(1, cdiv(W, p.conc));
+      int64_t hi = p.conc > d->batch ? cdiv(W, p.conc - d->batch) : p.tps_max;
+      hi = std::min<int64_t>(std::max(hi, lo), p.tps_max);
+      lo = std::min(lo, hi);
+      while (lo < hi) {
+        const int64_t mid = (lo + hi) / 2;
+        if (count(mid) <= p.conc) hi = mid;
+        else lo = mid + 1;
+      }
+      const int64_t tgt = lo;
       for (int b = 0; b < d->batch; ++b) {
         const int64_t sb = std::min<int64_t>(p.splits, cdiv(tl[b], tgt));
         if (cdiv(tl[b], sb) > p.tps_max) return bad("ordered split of %lld tiles", (long long)cdiv(tl[b], sb));
@@ -1061,8 +1085,7 @@ int32_t spec_debug_check_plan(const spec_dims* d, int32_t mode, int32_t T, int64
       }
       if (n_items > p.items) return bad("%lld splits for %d items", (long long)n_items, p.items);
     }
-    if ((uint64_t)d->n_kv_heads * p.n_rb * p.items > (uint64_t)groups * p.splits)
-      return bad("item slots overrun the split partials");
+    if (p.items < 1) return bad("no work items");
   }
   if (grid_size(d, p) > kMaxGrid) return bad("grid");
   return 0;

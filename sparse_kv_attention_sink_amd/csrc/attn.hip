@@ -380,14 +380,16 @@ void attn_bf16_kernel(AttnArgs a) {
   if constexpr (MODE == kVerify && WK == 1) {
     if (a.ordered) {
       // Balanced splits, longest first.  Every workgroup reads all the
-      // sequences' lengths and derives the same plan: with W tiles in the
-      // batch (per KV head) and `conc` workgroups of a (KV head, row block)
-      // running at once, a split takes about T = W / conc tiles (clamped to
-      // [tps, tps_max]), sequence b gets ceil(tiles_b / T) equal splits, and
-      // the splits are numbered as work items in order of size, largest
-      // first (ties: smaller sequence index), so that the hardware starts the
-      // longest work first.  Workgroup j of a KV head takes item j; items past
-      // the last split exit.
+      // sequences' lengths and derives the same plan: with `conc`
+      // workgroups of a (KV head, row block) running at once, a split takes
+      // at most T tiles, T the smallest value whose splits, min(S,
+      // ceil(tiles_b / T)) for sequence b, number at most conc (so that
+      // every split runs in the first round), at most tps_max; sequence b
+      // gets that many equal splits, and the splits are numbered as work
+      // items in order of size, largest first (ties: smaller sequence
+      // index), so that the hardware starts the longest work first.
+      // Workgroup j of a KV head takes item j; items past the last split
+      // exit.
       // (the tile ring is free until the first copies: it holds the plan)
       static_assert(Cf::RING >= 3 * kMaxOrderBatch * 4, "the ring holds the ordered plan");
       int32_t* const tl_s = reinterpret_cast<int32_t*>(ring);   // tiles per sequence
@@ -408,7 +410,33 @@ void attn_bf16_kernel(AttnArgs a) {
       if (threadIdx.x == 0) sel_s[0] = -1;
       __syncthreads();
       const int W = red_s[0] + red_s[1] + red_s[2] + red_s[3];
-      const int tgt = min(a.tps_max, max(a.tps, (W + a.conc - 1) / a.conc));
+      // T is sought in [ceil(W / conc), ceil(W / (conc - B))], W the batch's
+      // tiles: below the first, uncapped splits would exceed conc, and from
+      // the second on ceil() adds at most one split per sequence.  Every wavefront runs the same binary search
+      // (a lane holds up to 4 sequences; the split count of a candidate is a
+      // wavefront sum), so no barrier is needed.
+      int lo = max(1, (W + a.conc - 1) / a.conc);
+      int hi = a.conc > a.B ? (W + a.conc - a.B - 1) / (a.conc - a.B) : a.tps_max;
+      hi = min(max(hi, lo), a.tps_max);
+      lo = min(lo, hi);
+      static_assert(kMaxOrderBatch <= 4 * 64, "four sequences per lane");
+      int tl_r[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int i = (int)(threadIdx.x & 63) + 64 * k;
+        tl_r[k] = i < a.B ? tl_s[i] : 0;
+      }
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        int c = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) c += tl_r[k] > 0 ? min(a.splits, (tl_r[k] + mid - 1) / mid) : 0;
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) c += __shfl_xor(c, m, 64);
+        if (c <= a.conc) hi = mid;
+        else lo = mid + 1;
+      }
+      const int tgt = lo;
       for (int i = threadIdx.x; i < a.B; i += 256) ns_s[i] = min(a.splits, (tl_s[i] + tgt - 1) / tgt);
       __syncthreads();
       const int item = unit / a.Hkv;

@@ -41,7 +41,7 @@ constexpr int kMaxSplits = kMergeFan * kMergeFan;
 constexpr int kMinPoolGroups = 8;             // (pair, row block) groups that make a chunk pool pay
 constexpr int kChunkTiles = 8;                 // tiles per dynamically taken chunk
 constexpr int kMaxOrderBatch = 256;            // tree verify: longest-first work order up to this batch
-constexpr int kOrderTiles = 384;               // tree verify (ordered): capacity tiles per planned split, at most
+constexpr int kOrderTiles = 64;                // tree verify (ordered): the finest split the plan allows, in tiles
 constexpr int kCompactSlices = 64;             // pad-scan workgroups per sequence (compaction)
 constexpr int kCompactScanSlots = 65536;       // compaction: longer pad rows are scanned in slices
 constexpr int kMaxSelectBlocks = 8192;         // candidate blocks one selection scores
