@@ -173,17 +173,26 @@ Plan bf16_plan(const spec_dims* d, int32_t T, int64_t tiles, bool gather, bool v
   p.splits = (int32_t)cdiv(tiles, p.tps);
   p.n_blk = (int32_t)cdiv(p.splits, kMergeFan);
   if (p.ordered) {
-    // The device takes T = clamp(total tiles / conc, tps, tps_max) tiles per
-    // split and gives sequence b ceil(tiles_b / T) splits (at most `splits`).
-    // While the batch's tiles cannot exceed conc * tps_max, T is never
-    // clamped from above, so the splits number at most conc + B: that many
-    // work items per (KV head, row block) cover every sequence.
+    // The device takes the smallest T <= tps_max (tiles per split) whose
+    // splits, min(splits, ceil(tiles_b / T)) for sequence b, number at most
+    // conc, searching up to ceil(W / (conc - B)) (W the batch's tiles), and
+    // the largest candidate if none does.  The work items per (KV head, row
+    // block) bound those splits from the capacity alone: conc when even
+    // T = tps_max gives at most conc splits, or when the search's upper end
+    // stays within tps_max (there ceil() adds at most one split per
+    // sequence to W / T <= conc - B); conc + B while the batch's tiles stay
+    // within conc * tps_max (then W / tps_max + B); otherwise one per
+    // (sequence, split).
     p.conc = (int32_t)std::max<int64_t>(1, kTargetWorkgroups / ((int64_t)d->n_kv_heads * p.n_rb));
     p.tps_max = kMaxPadWords;
-    const int64_t all = (int64_t)d->batch * p.splits;
-    p.items = (int32_t)((int64_t)d->batch * tiles <= (int64_t)p.conc * p.tps_max
-                            ? std::min<int64_t>(all, (int64_t)d->batch + p.conc)
-                            : all);
+    const int64_t B = d->batch, all = B * p.splits;
+    if (B * std::min<int64_t>(p.splits, cdiv(tiles, p.tps_max)) <= p.conc ||
+        (p.conc > B && cdiv(B * tiles, p.conc - B) <= p.tps_max))
+      p.items = (int32_t)std::min<int64_t>(all, p.conc);
+    else if (B * tiles <= (int64_t)p.conc * p.tps_max)
+      p.items = (int32_t)std::min<int64_t>(all, B + p.conc);
+    else
+      p.items = (int32_t)all;
     // The kernel addresses a (KV head, row block)'s item partials with
     // 32-bit signed byte offsets.  A batch whose items overflow them (only
     // at hundreds of millions of cached keys) keeps the plain split order,
