@@ -11,9 +11,14 @@
 // One kernel.  Each block scans a contiguous slice of one logits row with
 // 16-byte loads and reduces (value, index) pairs under the rule "larger value
 // wins, NaN beats every number, ties go to the smaller index"; the slice's
-// winner lands in the workspace.  The block that finishes a sequence's rows
-// last (arrival counter per sequence) finishes the argmax of every row and
-// walks the tree in node order (parents precede children).
+// winner lands in the workspace.  The block that finishes a row's slices last
+// (arrival counter per row) merges them into the row's argmax, and the block
+// that finishes a sequence's rows last (arrival counter per sequence) walks
+// the tree in node order (parents precede children).  Two levels keep the
+// arrivals on one counter few (a sequence of 4 rows in 31 slices each had
+// 124 on one address); where the counter region cannot hold a counter per
+// row, the per-sequence counter takes every slice's arrival and the walk
+// merges the slices.
 #include "dev_common.h"
 
 namespace spec {
@@ -176,24 +181,57 @@ __device__ void accept_walk(int b, int N, int vsplits, __amdgpu_buffer_rsrc_t pr
   }
 }
 
+// part: [rows][vsplits] slice winners, then [rows] row winners (two
+// levels); counters: [B] per sequence, then [rows] per row (two levels).
 __global__ __launch_bounds__(256) void accept_kernel(
-    const float* __restrict__ logits, int64_t V, int N, int vsplits, int64_t vchunk,
+    const float* __restrict__ logits, int64_t V, int N, int vsplits, int64_t vchunk, int two_level,
     ArgBest* __restrict__ part, uint32_t* counters, const int32_t* __restrict__ tokens,
     const int32_t* __restrict__ parents, int64_t par_sb, int max_depth, int32_t* accept_len,
     int32_t* accept_path, int32_t* bonus, uint32_t* err) {
   const int row = blockIdx.x / vsplits, sp = blockIdx.x % vsplits;
+  const int rows = (int)(gridDim.x / vsplits), B = rows / (N + 1);
   const int b = row / (N + 1);
   const int64_t v0 = (int64_t)sp * vchunk;
   const int64_t v1 = min(V, v0 + vchunk);
   const ArgBest best = slice_argmax(logits + (int64_t)row * V, v0, v1);
   const __amdgpu_buffer_rsrc_t prs = coherent_rsrc(part, (uint32_t)(gridDim.x * sizeof(ArgBest)));
-  if (threadIdx.x == 0) {
-    store_sc1_f1(prs, (uint32_t)(blockIdx.x * sizeof(ArgBest)), best.v);
-    store_sc1_f1(prs, (uint32_t)(blockIdx.x * sizeof(ArgBest) + 4), __int_as_float(best.i));
+  const __amdgpu_buffer_rsrc_t rrs = coherent_rsrc(part + gridDim.x, (uint32_t)(rows * sizeof(ArgBest)));
+  auto store_best = [&](__amdgpu_buffer_rsrc_t rs, int i, float v, int idx) __attribute__((always_inline)) {
+    store_sc1_f1(rs, (uint32_t)(i * sizeof(ArgBest)), v);
+    store_sc1_f1(rs, (uint32_t)(i * sizeof(ArgBest) + 4), __int_as_float(idx));
+  };
+  if (!two_level) {
+    if (threadIdx.x == 0) store_best(prs, blockIdx.x, best.v, best.i);
+    if (!arrive_last(counters + b, (N + 1) * vsplits)) return;
+    accept_walk(b, N, vsplits, prs, tokens, parents, par_sb, max_depth, accept_len, accept_path,
+                bonus, err);
+    return;
   }
-  if (!arrive_last(counters + b, (N + 1) * vsplits)) return;
-  accept_walk(b, N, vsplits, prs, tokens, parents, par_sb, max_depth, accept_len, accept_path,
-              bonus, err);
+  if (vsplits == 1) {
+    if (threadIdx.x == 0) store_best(rrs, row, best.v, best.i);
+  } else {
+    if (threadIdx.x == 0) store_best(prs, blockIdx.x, best.v, best.i);
+    if (!arrive_last(counters + B + row, vsplits)) return;
+    if (threadIdx.x < 64) {   // the row's slices (at most 64), one per lane
+      float bv = -INFINITY;
+      int bi = INT_MAX;
+      if ((int)threadIdx.x < vsplits) {
+        const uint32_t o = (uint32_t)((row * vsplits + threadIdx.x) * sizeof(ArgBest));
+        bv = load_sc1_f1(prs, o);
+        bi = __float_as_int(load_sc1_f1(prs, o + 4));
+      }
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) {
+        const float ov = __shfl_xor(bv, m, 64);
+        const int oi = __shfl_xor(bi, m, 64);
+        arg_consider(bv, bi, ov, oi);
+      }
+      if (threadIdx.x == 0) store_best(rrs, row, bv, bi);
+    }
+  }
+  if (!arrive_last(counters + b, N + 1)) return;
+  accept_walk(b, N, 1, rrs, tokens, parents, par_sb, max_depth, accept_len, accept_path, bonus,
+              err);
 }
 
 size_t accept_part_offset(int) { return kScratchOff; }
@@ -201,15 +239,15 @@ size_t accept_part_offset(int) { return kScratchOff; }
 hipError_t launch_accept(int B, int N, int V, const float* logits, const int32_t* tokens,
                          const int32_t* parents, int64_t parents_sb, int max_depth,
                          int32_t* accept_len, int32_t* accept_path, int32_t* bonus, void* ws,
-                         int vsplits, hipStream_t st, uint32_t* err) {
+                         int vsplits, int two_level, hipStream_t st, uint32_t* err) {
   uint8_t* w = reinterpret_cast<uint8_t*>(ws);
   uint32_t* counters = reinterpret_cast<uint32_t*>(w + kHeaderBytes);
   ArgBest* part = reinterpret_cast<ArgBest*>(w + accept_part_offset(B));
   const int64_t vchunk = cdiv(V, vsplits);
   const int64_t rows = (int64_t)B * (N + 1);
   hipLaunchKernelGGL(accept_kernel, dim3((unsigned)(rows * vsplits)), dim3(256), 0, st, logits,
-                     (int64_t)V, N, vsplits, vchunk, part, counters, tokens, parents, parents_sb,
-                     max_depth, accept_len, accept_path, bonus, err);
+                     (int64_t)V, N, vsplits, vchunk, two_level, part, counters, tokens, parents,
+                     parents_sb, max_depth, accept_len, accept_path, bonus, err);
   return hipGetLastError();
 }
 

@@ -284,11 +284,14 @@ Plan verify_plan(const spec_dims* d, int32_t N, int32_t capacity) {
   return f32_plan(d, N, std::max(capacity, 1), true);
 }
 
-// Slices per logits row: as many as keep every block resident in one round
-// (8 blocks of 256 threads per CU), so no straggler round runs alone at the
-// end, and at least 4096 values per slice.
+// Slices per logits row: about two rounds of resident blocks (8 blocks of
+// 256 threads per CU), at least 4096 values per slice.  (One round, so that
+// no straggler round runs alone at the end, took the 16K batch of 8 from 60
+// to 52 us with one arrival counter per sequence; with a counter per row,
+// two rounds of smaller slices measured 52.2 against 53.9 us there and 94.5
+// against 100.2 us on the ragged batch of 16.)
 int accept_vsplits(int64_t rows, int64_t V) {
-  int64_t vs = kTargetWorkgroups * 4 / (rows > 0 ? rows : 1);
+  int64_t vs = kTargetWorkgroups * 8 / (rows > 0 ? rows : 1);
   int64_t vmax = V / 4096;
   if (vmax < 1) vmax = 1;
   if (vs > vmax) vs = vmax;
@@ -304,8 +307,15 @@ size_t select_bytes(const spec_dims* d, int32_t max_blocks) {
 
 // header | counter region (one arrival counter per sequence first) |
 // (value, index) winner per slice
+// Per-row arrival counters (two levels) fit the counter region beside the
+// per-sequence ones, and a row's slices fit one wavefront's merge.
+bool accept_two_level(int64_t batch, int64_t rows, int vs) {
+  return batch + rows <= (int64_t)kCounterWords && vs <= 64;
+}
+
+// header | counters | slice winners [rows][vs] | row winners [rows] (8 bytes each)
 size_t accept_bytes(int64_t, int64_t rows, int vs) {
-  return align_up(kScratchOff + (size_t)rows * vs * 8, 256);
+  return align_up(kScratchOff + (size_t)rows * (vs + 1) * 8, 256);
 }
 
 int64_t draft_max_view(const spec_kv* cache, int32_t Tq, int32_t n_sink, int32_t window,
@@ -656,6 +666,7 @@ spec_status spec_accept_greedy(int32_t batch, int32_t n_nodes, int32_t vocab, co
   if (rows * vs > kMaxGrid) return fail(SPEC_E_UNSUPPORTED, "problem too large for one launch");
   hipError_t e = launch_accept(batch, n_nodes, vocab, logits, draft_tokens, parents, parents_stride_b,
                                max_depth, accept_len, accept_path, bonus, workspace, vs,
+                               accept_two_level(batch, rows, vs) ? 1 : 0,
                                static_cast<hipStream_t>(stream), static_cast<uint32_t*>(workspace));
   if (e != hipSuccess) return hip_fail(e, "accept launch");
   return SPEC_OK;

@@ -227,7 +227,7 @@ hipError_t launch_combine(const AttnArgs& a, int dtype, hipStream_t st);
 hipError_t launch_accept(int B, int N, int V, const float* logits, const int32_t* tokens,
                          const int32_t* parents, int64_t parents_sb, int max_depth,
                          int32_t* accept_len, int32_t* accept_path, int32_t* bonus,
-                         void* ws, int vsplits, hipStream_t st, uint32_t* err);
+                         void* ws, int vsplits, int two_level, hipStream_t st, uint32_t* err);
 hipError_t launch_kv_commit(const CommitArgs& a, hipStream_t st);
 hipError_t launch_kv_compact(const CompactArgs& a, hipStream_t st);
 hipError_t launch_block_means(const MeansArgs& a, hipStream_t st);

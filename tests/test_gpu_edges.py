@@ -439,7 +439,10 @@ def accept_corner_case(V, seed):
     return logits, tokens, par.astype(np.int32)
 
 
-@pytest.mark.parametrize("V", [1, 7, 1001, 128256])
+# (1, 7, 1001: one slice per row; 128,256: 31 slices merged per row, then per
+# sequence; 300,001: 73 slices, more than one wavefront merges, so every
+# slice arrives on the sequence's counter and the walk merges them)
+@pytest.mark.parametrize("V", [1, 7, 1001, 128256, 300001])
 def test_accept_corner_cases_bit_exact(V):
     logits, tokens, par = accept_corner_case(V, V)
     got = skg.spec_accept_greedy(dev(logits), dev(tokens), dev(par), 4)
