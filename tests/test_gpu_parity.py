@@ -478,6 +478,31 @@ def test_verify_longest_first_with_empty_splits_and_two_merge_levels():
     np.testing.assert_array_equal(pos, oracle.position_ids(case.cache_len, pad, tree.parents))
 
 
+def test_verify_one_long_sequence_among_many_short_ones():
+    """A skewed batch for the balanced plan: one sequence of 40,000 keys and
+    63 of at most 100, with pads; the search for the split size gives the
+    long sequence the most splits its plan allows while the short ones keep
+    one each, and every split runs at once."""
+    B, Hq, Hkv, D, cap = 64, 8, 2, 128, 40000
+    rng = np.random.default_rng(9500)
+    lens = [cap] + [int(x) for x in rng.integers(0, 101, size=B - 1)]
+    tree = synth.layered_tree(rng, (10, 18, 18, 18))
+    N = tree.n
+    case = synth.make_attn_case(9501, B=B, Hq=Hq, Hkv=Hkv, D=D, L_cap=cap, T=N, cache_len=lens,
+                                dtype="bf16", value_scale=1.0)
+    tk = synth.draw_normal(rng, (B, Hkv, N, D), 1.0, "bf16")
+    tv = synth.draw_normal(rng, (B, Hkv, N, D), 1.0, "bf16")
+    pad = np.zeros((B, cap), dtype=np.uint8)
+    for b in range(B):
+        pad[b, :lens[b]] = synth.pad_groups(rng, lens[b], n_groups=3, group=4)
+    got, lse, pos = run_verify(case, case.q, tk, tv, tree.parents, pad=pad)
+    ref, lse_ref = oracle.verify_attn_ref(case.q, case.k, case.v, case.cache_len, tk, tv,
+                                          tree.parents, scale=case.scale, pad=pad)
+    assert_close(got, ref, "bf16", "skewed batch verify")
+    assert_lse_close(lse, lse_ref, 1e-3, "skewed batch verify lse")
+    np.testing.assert_array_equal(pos, oracle.position_ids(case.cache_len, pad, tree.parents))
+
+
 @pytest.mark.parametrize("B,Hq,Hkv", [(300, 8, 2), (256, 4, 1)])
 def test_verify_batch_at_and_above_the_ordered_limit(B, Hq, Hkv):
     """A batch of 300 (above the 256 that the longest-first order ranks)
