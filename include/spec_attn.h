@@ -87,7 +87,7 @@ typedef int32_t spec_status;
 enum {
   SPEC_OK = 0,
   SPEC_E_INVALID = -1,       /* bad argument: null pointer, shape, stride, alignment */
-  SPEC_E_UNSUPPORTED = -2,   /* well-formed but outside what this build supports */
+  SPEC_E_UNSUPPORTED = -2,   /* well-formed but outside what the library supports */
   SPEC_E_WORKSPACE = -3,     /* workspace missing or smaller than required */
   SPEC_E_HIP = -4,           /* the HIP runtime reported an error */
   SPEC_E_DEVICE_RANGE = -5   /* a kernel found an out-of-range device value */
