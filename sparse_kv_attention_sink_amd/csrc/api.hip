@@ -1070,14 +1070,28 @@ int32_t spec_debug_check_plan(const spec_dims* d, int32_t mode, int32_t T, int64
     if ((int64_t)p.items * p.rb * d->head_dim * 4 > INT32_MAX)
       return bad("%d item partials exceed 32-bit offsets", p.items);
     const int64_t cap_tiles = cdiv(extent, kTileKeys), nt = cdiv(T, kTileKeys);
-    for (int pattern = 0; pattern < 4; ++pattern) {
+    // (patterns: all full, all empty, one full, a linear ramp, then
+    // pseudo-random lengths: uniform, cubed toward short, and a mix of full
+    // and near-empty sequences)
+    uint64_t rs = 0x9e3779b97f4a7c15ull ^ ((uint64_t)d->batch << 32) ^ (uint64_t)cap_tiles;
+    const auto rnd = [&]() {   // xorshift64, values in [0, 1)
+      rs ^= rs << 13;
+      rs ^= rs >> 7;
+      rs ^= rs << 17;
+      return (double)(rs >> 11) / 9007199254740992.0;
+    };
+    for (int pattern = 0; pattern < 10; ++pattern) {
       int64_t W = 0, n_items = 0;
       std::vector<int64_t> tl(d->batch);
       for (int b = 0; b < d->batch; ++b) {
+        const double u = pattern >= 4 ? rnd() : 0.0;
         const int64_t len_tiles = pattern == 0 ? cap_tiles
                                 : pattern == 1 ? 0
                                 : pattern == 2 ? (b == 0 ? cap_tiles : 0)
-                                               : (cap_tiles * (b + 1)) / d->batch;
+                                : pattern == 3 ? (cap_tiles * (b + 1)) / d->batch
+                                : pattern % 3 == 1 ? (int64_t)(u * (double)(cap_tiles + 1))
+                                : pattern % 3 == 2 ? (int64_t)(u * u * u * (double)(cap_tiles + 1))
+                                                   : (u < 0.2 ? cap_tiles : (int64_t)(u * 0.02 * (double)cap_tiles));
         tl[b] = len_tiles + nt;
         W += tl[b];
       }
