@@ -450,6 +450,96 @@ def test_verify_of_193_to_256_rows(D, Hq, Hkv, widths):
     np.testing.assert_array_equal(pos, oracle.position_ids(case.cache_len, pad, tree.parents))
 
 
+# ------------------------------------------------------------ drawn shapes
+# Seeded draws across the shapes the planner distinguishes: rows per
+# (sequence, KV head) from 1 to 512 (every row-block shape and wavefront
+# count), head_dim 64 and 128, batches up to 24 with lengths from empty to
+# full, random trees, pads.
+
+def _drawn_verify_case(i):
+    rng = np.random.default_rng(9700 + i)
+    D = int(rng.choice([64, 128]))
+    Hkv = int(rng.choice([1, 2, 4]))
+    G = int(rng.choice([1, 2, 4, 8]))
+    depth = int(rng.integers(1, 6))
+    widths = [int(x) for x in rng.integers(1, 14, size=depth)]
+    if i % 6 == 5:   # (every sixth: 8 query heads per KV head and 25 to 64 nodes)
+        G = 8
+        widths = [int(x) for x in rng.integers(5, 17, size=4)]
+    while sum(widths) > 64:
+        widths[int(np.argmax(widths))] -= 1
+    B = int(rng.integers(1, 25))
+    cap = int(rng.integers(1, 2049))
+    lens = rng.integers(0, cap + 1, size=B)
+    lens[rng.random(B) < 0.2] = cap
+    return rng, D, Hkv, G, widths, B, cap, [int(x) for x in lens]
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_verify_drawn_shapes(i):
+    rng, D, Hkv, G, widths, B, cap, lens = _drawn_verify_case(i)
+    tree = synth.layered_tree(rng, widths)
+    N = tree.n
+    case = synth.make_attn_case(9800 + i, B=B, Hq=Hkv * G, Hkv=Hkv, D=D, L_cap=cap, T=N,
+                                cache_len=lens, dtype="bf16", value_scale=1.0)
+    tk = synth.draw_normal(rng, (B, Hkv, N, D), 1.0, "bf16")
+    tv = synth.draw_normal(rng, (B, Hkv, N, D), 1.0, "bf16")
+    pad = None
+    if rng.random() < 0.7:
+        pad = np.zeros((B, (cap + 3) // 4 * 4), dtype=np.uint8)   # rows: a multiple of 4 bytes
+        for b in range(B):
+            pad[b, :lens[b]] = synth.pad_groups(rng, lens[b], n_groups=int(rng.integers(0, 40)),
+                                                group=int(rng.integers(2, 7)))
+    got, lse, pos = run_verify(case, case.q, tk, tv, tree.parents, pad=pad)
+    ref, lse_ref = oracle.verify_attn_ref(case.q, case.k, case.v, case.cache_len, tk, tv,
+                                          tree.parents, scale=case.scale, pad=pad)
+    what = f"drawn verify {i}: B={B} Hkv={Hkv} G={G} D={D} N={N} rows={N * G} cap={cap}"
+    assert_close(got, ref, "bf16", what)
+    assert_lse_close(lse, lse_ref, 1e-3, what + " lse")
+    np.testing.assert_array_equal(pos, oracle.position_ids(case.cache_len, pad, tree.parents))
+
+
+def _drawn_draft_case(i):
+    rng = np.random.default_rng(9900 + i)
+    D = int(rng.choice([64, 128]))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    G = int(rng.choice([1, 2, 4, 8]))
+    T = int(rng.choice([1, 1, 2, 3, 5, 9, 17, 33]))
+    B = int(rng.integers(1, 17))
+    cap = int(rng.integers(T, 3001))
+    lens = rng.integers(T, cap + 1, size=B)
+    lens[rng.random(B) < 0.2] = cap
+    return rng, D, Hkv, G, T, B, cap, [int(x) for x in lens]
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_draft_drawn_shapes(i):
+    """Window drafts (sink and window drawn, including none and longer than
+    the cache) and budget drafts (lists per KV head or shared, with -1
+    padding and repeats) on drawn shapes."""
+    rng, D, Hkv, G, T, B, cap, lens = _drawn_draft_case(i)
+    case = synth.make_attn_case(9950 + i, B=B, Hq=Hkv * G, Hkv=Hkv, D=D, L_cap=cap, T=T,
+                                cache_len=lens, dtype="bf16", value_scale=1.0)
+    what = f"drawn draft {i}: B={B} Hkv={Hkv} G={G} D={D} T={T} rows={T * G} cap={cap}"
+    if i % 2 == 0:
+        sink = int(rng.choice([0, 1, 4, 16]))
+        win = int(rng.choice([1, 7, 64, 500, 4000]))
+        got, lse = run_draft(case, n_sink=sink, window=win)
+        ref, lse_ref = oracle.draft_attn_ref(case.q, case.k, case.v, case.cache_len,
+                                             scale=case.scale, n_sink=sink, window=win)
+    else:
+        budget = int(rng.integers(1, 2500))
+        hidx = 1 if rng.random() < 0.3 else Hkv
+        idx = np.stack([rng.integers(0, max(1, lens[b] - T + 1), size=(hidx, budget))
+                        for b in range(B)]).astype(np.int32)
+        idx[rng.random(idx.shape) < 0.1] = -1
+        got, lse = run_draft(case, idx=idx)
+        ref, lse_ref = oracle.draft_attn_ref(case.q, case.k, case.v, case.cache_len,
+                                             scale=case.scale, idx=idx)
+    assert_close(got, ref, "bf16", what)
+    assert_lse_close(lse, lse_ref, 1e-3, what + " lse")
+
+
 # ------------------------------------------------------------ tree-verify work order
 
 def test_verify_longest_first_with_empty_splits_and_two_merge_levels():
