@@ -105,8 +105,9 @@ Plan bf16_plan(const spec_dims* d, int32_t T, int64_t tiles, bool gather, bool v
     // Up to 128 rows take one or two 16-row tiles per wavefront, more rows
     // row blocks of 128 or 192 (two or three tiles per wavefront; four would
     // need more registers than two wavefronts per SIMD allow).  Every row
-    // block reads every tile, and three tiles per wavefront cost about a
-    // third more per (row, key) than two, so blocks of 192 are taken where
+    // block reads every tile, and three tiles per wavefront cost more per
+    // (row, key) than two (about 17% more cycles per MFMA flop on the
+    // ragged batch of 16), so blocks of 192 are taken where
     // they save a block and were measured to pay: 129 to 192 rows (a
     // 44-node tree with 4 query heads per KV head: 176; the 16K batch of 8:
     // 159.4 -> 148.8 us, the ragged batch of 16: 321.7 -> 295.0 us) and 257
