@@ -147,3 +147,32 @@ def test_one_workspace_serves_every_call_kind_and_shape():
     # every counter is back at zero
     counters = shared[256:256 + (1 << 20)]
     assert int(counters.count_nonzero()) == 0
+
+
+def test_calls_on_separate_streams_with_separate_workspaces():
+    """Every kind of call at once, each on a stream and a workspace of its
+    own, three rounds: the calls share no hidden state (counters, scratch)
+    beyond their workspaces, so every output equals, bit for bit, the same
+    call run alone."""
+    calls = _calls()
+    alone = []
+    for name, fn, nbytes in calls:
+        alone.append(_bits(fn(skg.new_workspace(nbytes, "cuda"))))
+        torch.cuda.synchronize()
+    main = torch.cuda.current_stream()
+    streams = [torch.cuda.Stream() for _ in calls]   # (default priority)
+    spaces = [skg.new_workspace(nbytes, "cuda") for _, _, nbytes in calls]
+    torch.cuda.synchronize()
+    for rnd in range(3):
+        outs = []
+        for (name, fn, _), st, ws in zip(calls, streams, spaces):
+            st.wait_stream(main)
+            with torch.cuda.stream(st):
+                outs.append(fn(ws))
+        for st in streams:
+            main.wait_stream(st)
+        torch.cuda.synchronize()
+        for (name, _, _), got, want in zip(calls, outs, alone):
+            assert _equal(_bits(got), want), f"round {rnd}: {name} differs when run beside the others"
+    for ws in spaces:
+        assert skg.spec_device_status(ws) == 0
