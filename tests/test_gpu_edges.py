@@ -231,7 +231,10 @@ def test_cache_whose_address_has_bit_31_of_its_low_word_set():
     tree = synth.layered_tree(np.random.default_rng(4), (4, 6, 8))       # 18 nodes: shared ring
     case = small_case(33, T=tree.n)
     nbytes = case.k.size * 2
-    pool = torch.empty((1 << 31) + 4 * nbytes + 4096, dtype=torch.uint8, device="cuda")
+    # (the pool spans a whole 4 GiB period of the low word, so the first
+    # offset whose low word is 2^31, rounded up to 256 bytes, lies inside it
+    # wherever the allocator puts the pool)
+    pool = torch.empty((1 << 32) + 4 * nbytes + 4096, dtype=torch.uint8, device="cuda")
     base = pool.data_ptr()
     off = (((1 << 31) - (base & 0xFFFFFFFF)) % (1 << 32) + 255) // 256 * 256
     assert off + 2 * nbytes <= pool.numel()
