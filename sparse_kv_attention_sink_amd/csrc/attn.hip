@@ -805,7 +805,23 @@ void attn_bf16_kernel(AttnArgs a) {
     } else if constexpr (MODE == kDraftGather) {
       pw = __builtin_amdgcn_readfirstlane(padbits_s[t - t0]);
     }
-    const bool full = !tree_tile && (t + 1) * kTileKeys <= n_view && !row_masks && pw == 0u;
+    bool full = !tree_tile && (t + 1) * kTileKeys <= n_view && pw == 0u;
+    if (row_masks) {
+      // Several window-draft queries: a tile is visible to every row when
+      // its last key precedes the first query (causal) and its window keys
+      // lie inside the last query's window (the sink always is); most
+      // window tiles are, and skip the per-row masks.  (view positions
+      // increase within a tile; uniform scalar tests)
+      bool all_rows = false;
+      if constexpr (MODE == kDraftWindow) {
+        const int v_first = t * kTileKeys, v_last = v_first + kTileKeys - 1;
+        const int p_last = v_last < s_len ? v_last : w_start + (v_last - s_len);
+        const int v_win = max(v_first, s_len);   // first window key of the tile
+        all_rows = p_last < L - T + 1 &&
+                   (v_win > v_last || w_start + (v_win - s_len) >= L - window_);
+      }
+      full = full && all_rows;
+    }
 
     // K fragments (A operand of S^T): key h*16 + l16, head-dim chunk cc*4 + q4;
     // V^T fragments (A operand of O^T) of d tile dt.
@@ -870,7 +886,7 @@ void attn_bf16_kernel(AttnArgs a) {
       }
     }
     int jpos[8];
-    if (row_masks) {
+    if (row_masks && !full) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int kk = (e >> 2) * 16 + q4 * 4 + (e & 3);
