@@ -1108,14 +1108,17 @@ void attn_bf16_kernel(AttnArgs a) {
       }
     }
   } else {
-    // merge the four wavefronts' running states through LDS
+    // merge the four wavefronts' running states through LDS (rows past the
+    // last one are neither written nor merged)
     __syncthreads();
     float* ms = reinterpret_cast<float*>(ring);   // [4][RC]
     float* ls = ms + 4 * RC;                      // [4][RC]
     float* os = ls + 4 * RC;                      // [4][RC][D]
+    const int rows_live = min(RC, a.R - z * RC);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       const int rl = rt * 16 + l16;
+      if (rl >= rows_live) continue;
       if (q4 == 0) {
         ms[wave * RC + rl] = m[rt];
         ls[wave * RC + rl] = lr[rt];
@@ -1125,7 +1128,7 @@ void attn_bf16_kernel(AttnArgs a) {
         *reinterpret_cast<f32x4*>(os + ((size_t)wave * RC + rl) * D + dt * 16 + q4 * 4) = acc[rt][dt];
     }
     __syncthreads();
-    for (int it = tid; it < RC * (D / 4); it += 256) {
+    for (int it = tid; it < rows_live * (D / 4); it += 256) {
       const int rl = it / (D / 4), d0 = (it % (D / 4)) * 4;
       float M = -INFINITY;
 #pragma unroll
