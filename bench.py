@@ -37,6 +37,7 @@ HBM_PEAK_GBS = 8000.0
 L1M, LAYERS, HQ, HKV, D, CHAIN, VOCAB = 1 << 20, 32, 32, 8, 128, 3, 128256
 SINK, WINDOW = 4, 4096
 ESZ = 2
+ACCEPT_16K_BYTES = 8 * 65 * VOCAB * 4   # the acceptance's fp32 logits, 16K batch of 8, 64 nodes
 
 
 def log(*a):
@@ -468,11 +469,24 @@ def run_probes(torch):
         del graph
         reads[f"wg{wg}"] = round(g_ms / len(bufs) * 1e3, 2)
     del bufs
+    # a one-pass read of the acceptance's logits at 16K (8 x 65 x 128,256
+    # fp32), rotating over 4 buffers (1.07 GB): what a read of that size
+    # reaches, ramp-up and tail included
+    mid = ACCEPT_16K_BYTES
+    mbufs = [torch.ones(mid // 2, dtype=torch.bfloat16, device=dev) for _ in range(4)]
+    mids = {}
+    for wg in (2048, 8192, 32768):
+        for inf in (8, 16):
+            g_ms, graph = graph_replay_ms(torch, lambda: [pr.read(b, wg, inf, sink) for b in mbufs], 4)
+            del graph
+            mids[f"regs_wg{wg}_inflight{inf}"] = round(mid / (g_ms / len(mbufs) * 1e-3) / 1e9, 1)
+    del mbufs
     torch.cuda.empty_cache()
     return {"stream_read_gbs": max(best_regs, best_lds), "stream_read_regs_gbs": best_regs,
             "stream_read_lds_gbs": best_lds, "stream_read_bytes": nbytes, "shapes": shapes,
             "empty_launch_us": {"1_workgroup": round(empty1, 2), "256_workgroups": round(empty256, 2)},
-            "read_16_8mb_us": reads, "read_16_8mb_floor_us": min(reads.values())}
+            "read_16_8mb_us": reads, "read_16_8mb_floor_us": min(reads.values()),
+            "read_267mb_gbs": mids, "read_267mb_best_gbs": max(mids.values())}
 
 
 def tree_verify_roofline(r16):
@@ -1191,7 +1205,8 @@ def main():
     probes = run_probes(torch)
     log(f"[bench] stream read {probes['stream_read_gbs']} GB/s (registers "
         f"{probes['stream_read_regs_gbs']}, LDS copies {probes['stream_read_lds_gbs']}); empty "
-        f"launch {probes['empty_launch_us']} us; 16.8 MB read {probes['read_16_8mb_floor_us']} us")
+        f"launch {probes['empty_launch_us']} us; 16.8 MB read {probes['read_16_8mb_floor_us']} us; "
+        f"267 MB read {probes['read_267mb_best_gbs']} GB/s")
     r1m, layers = run_1m(args, torch, skg)
     log(f"[bench] 1M step: {r1m['ms_step']:.3f} ms, {r1m['gbs']:.1f} GB/s")
     cpu = None
@@ -1246,6 +1261,10 @@ def main():
             vs_stream[f"accept_{tag}"] = round(r["256"]["accept_gbs"] / ceil, 4)
     for tree_name in ("tree44", "tree64"):
         vs_stream[f"ragged_verify_{tree_name}"] = round(rrag[tree_name]["verify_gbs"] / ceil, 4)
+    if r16:
+        # the acceptance against a plain read of its own size (the 4 GiB
+        # ceiling leaves out a 267 MB read's ramp-up and tail)
+        vs_stream["accept_16k_vs_same_size_read"] = round(r16["256"]["accept_gbs"] / probes["read_267mb_best_gbs"], 4)
     floor = probes["read_16_8mb_floor_us"]
     draft_floor = {"read_16_8mb_floor_us": floor,
                    "empty_launch_us": probes["empty_launch_us"]["256_workgroups"],
