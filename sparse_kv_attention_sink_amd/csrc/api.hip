@@ -145,6 +145,12 @@ Plan bf16_plan(const spec_dims* d, int32_t T, int64_t tiles, bool gather, bool v
   // than the cross-workgroup merge a second split brings (a budget of 256 of
   // the 16K batch of 8: 10.2 -> 8.0 us per call, device time).
   if (p.wk == 4 && !verify && tiles <= 16) S = 1;
+  // Window drafts take at most 12 splits: the final merge reads every
+  // split's partial, and with 12 splits the deepest wavefront still streams
+  // as many tiles as with 16 (the 1M drafts' 129 tiles over 8 KV heads, in
+  // device time: 3 queries 13.8 -> 13.3 us, 1 query 10.8 -> 10.7 us; 8, 10,
+  // 11 and 14 splits measured slower than 12).
+  if (p.wk == 4 && !verify && !gather) S = std::min<int64_t>(S, 12);
   // A tree verify sizes its splits on the device from the sequences' own
   // lengths (see the kernel), at most S per sequence: S allows splits of
   // kOrderTiles tiles over the capacity (up to one merge level of 16), so
