@@ -140,11 +140,13 @@ Plan bf16_plan(const spec_dims* d, int32_t T, int64_t tiles, bool gather, bool v
   int64_t lo = 1;
   if (gather) lo = std::max(lo, cdiv(tiles, kMaxGatherKeys / kTileKeys));
   if (verify) lo = std::max(lo, cdiv(tiles, kMaxPadWords));
-  // A draft whose (sequence, KV head) spans at most 16 tiles runs as one
-  // split: its four wavefronts stream up to four tiles each, which costs less
+  // A draft whose (sequence, KV head) spans at most 8 tiles runs as one
+  // split: its four wavefronts stream up to two tiles each, which costs less
   // than the cross-workgroup merge a second split brings (a budget of 256 of
-  // the 16K batch of 8: 10.2 -> 8.0 us per call, device time).
-  if (p.wk == 4 && !verify && tiles <= 16) S = 1;
+  // the 16K batch of 8: 10.2 -> 8.0 us per call, device time).  With 16
+  // tiles (a budget of 512) four tiles per wavefront cost more than the
+  // merge: 11.1 -> 10.2 us split.
+  if (p.wk == 4 && !verify && tiles <= 8) S = 1;
   // Window drafts take at most 12 splits: the final merge reads every
   // split's partial, and with 12 splits the deepest wavefront still streams
   // as many tiles as with 16 (the 1M drafts' 129 tiles over 8 KV heads, in
