@@ -219,6 +219,35 @@ def test_ragged_verify_sampled(ragged):
         assert_lse_close(lse[sl], lse_ref, 1e-3, "ragged verify lse")
 
 
+def test_verify_batch_of_64_at_16k_sampled():
+    """64 padded sequences of 12,000 to 16,384 keys with the 64-node tree:
+    more sequences than the workgroups of a KV head that run at once, so
+    every sequence is one split (1,024 workgroups, two rounds).  Four
+    sampled (sequence, KV head) pairs against the oracle, every position
+    exact."""
+    d = dg.ragged_batch((10, 18, 18, 18), B=64, lo=12000, hi=16384, seed=synth.SEEDS[5] + 64)
+    B, N = len(d["lens"]), d["tree"].n
+    cl = torch.from_numpy(d["lens"]).cuda()
+    pad = torch.from_numpy(d["pad"]).cuda()
+    par = torch.from_numpy(d["tree"].parents).cuda()
+    out, lse, pos = skg.spec_attn_verify_tree(d["verify_q"], d["k"], d["v"], cl, d["tree_k"],
+                                              d["tree_v"], par, pad=pad)
+    torch.cuda.synchronize()
+    got = host64(out)
+    lse = lse.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got))
+    np.testing.assert_array_equal(pos.cpu().numpy(),
+                                  oracle.position_ids(d["lens"], d["pad"], d["tree"].parents))
+    longest = int(np.argmax(d["lens"]))
+    for b, g in [(0, 0), (longest, 3), (31, 5), (B - 1, 7)]:
+        ref, lse_ref = verify_pair_ref(d, b, g, int(d["lens"][b]), d["tree"].parents, d["pad"])
+        sl = (slice(b, b + 1), slice(None), slice(g * G, (g + 1) * G))
+        assert_close(got[sl], ref, "bf16", f"batch 64 verify pair ({b}, {g})")
+        assert_lse_close(lse[sl], lse_ref, 1e-3, "batch 64 verify lse")
+    del d, out
+    torch.cuda.empty_cache()
+
+
 def test_ragged_accept(ragged):
     tree = ragged["tree"]
     a = synth.make_accept_case(synth.SEEDS[5] + tree.n, tree, 16, 128256)
